@@ -1,0 +1,241 @@
+"""Python binding of the MI355X ring-attention step library (``libringattn.so``).
+
+Argument marshalling only: every step of the forward, merge and backward runs
+in the library's HIP kernels on gfx950.  PyTorch is used for device memory and
+streams; tensors are passed by ``data_ptr()`` and the caller's current HIP
+stream.  If the shared library has not been built the import of the native
+functions fails loudly -- there is no CPU fallback.
+
+The low-level functions carry the C ABI's names and parameters
+(``ring_attn_fwd``, ``ring_attn_fwd_f32``, ``ring_attn_merge``,
+``ring_attn_bwd``, ``ring_attn_bwd_f32``, ...).  ``fwd``, ``bwd`` and
+``merge`` are conveniences that read sizes from tensor shapes, allocate the
+outputs and pick the bf16 or fp32 entry point from the input dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libringattn.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_OOM = range(5)
+PROFILE_KINDS = ("fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "merge", "copy")
+
+EXPORTED = (
+    "ring_attn_fwd", "ring_attn_fwd_f32", "ring_attn_merge", "ring_attn_bwd", "ring_attn_bwd_f32",
+    "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
+    "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
+)
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"ring_attn error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libringattn.so`` (built by ``long_context_exact_ring_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_exact_ring_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    fwd_args = [vp, vp, vp, i, i, i, i, i, i, i, f32p, f32p, vp]
+    for name in ("ring_attn_fwd", "ring_attn_fwd_f32"):
+        fn = getattr(L, name)
+        fn.argtypes = fwd_args
+        fn.restype = i
+    bwd_args = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp]
+    for name in ("ring_attn_bwd", "ring_attn_bwd_f32"):
+        fn = getattr(L, name)
+        fn.argtypes = bwd_args
+        fn.restype = i
+    L.ring_attn_merge.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp, vp]
+    L.ring_attn_merge.restype = i
+    L.ring_attn_last_error.argtypes = []
+    L.ring_attn_last_error.restype = ctypes.c_char_p
+    L.ring_attn_workspace_bytes.argtypes = [i, i, i, i]
+    L.ring_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.ring_attn_profile_enable.argtypes = [i]
+    L.ring_attn_profile_enable.restype = i
+    L.ring_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.ring_attn_profile_read.restype = i
+    L.ring_attn_schedule.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_int), i]
+    L.ring_attn_schedule.restype = i
+    L.ring_attn_debug.argtypes = [i, ctypes.c_longlong]
+    L.ring_attn_debug.restype = i
+    L.ring_attn_shutdown.argtypes = []
+    L.ring_attn_shutdown.restype = None
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _addr(x) -> Optional[int]:
+    """Device address of a tensor (or a raw integer address / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _ptr_array(xs: Sequence) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(1, len(xs)))()
+    for j, x in enumerate(xs):
+        arr[j] = _addr(x)
+    return arr
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != RA_OK:
+        msg = lib().ring_attn_last_error()
+        raise RingAttnError(rc, msg.decode() if msg else "")
+
+
+def last_error() -> str:
+    msg = lib().ring_attn_last_error()
+    return msg.decode() if msg else ""
+
+
+# ------------------------------------------------------------------ C-ABI mirrors
+def ring_attn_fwd(q, k_blocks, v_blocks, n_blocks, block_len, heads, kv_heads, head_dim, causal, rank,
+                  out, lse, stream=None) -> int:
+    """bf16 forward ring step; returns the C status code (no exception)."""
+    return lib().ring_attn_fwd(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks, block_len,
+                               heads, kv_heads, head_dim, int(bool(causal)), rank, _addr(out), _addr(lse),
+                               _stream(stream))
+
+
+def ring_attn_fwd_f32(q, k_blocks, v_blocks, n_blocks, block_len, heads, kv_heads, head_dim, causal, rank,
+                      out, lse, stream=None) -> int:
+    return lib().ring_attn_fwd_f32(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks,
+                                   block_len, heads, kv_heads, head_dim, int(bool(causal)), rank, _addr(out),
+                                   _addr(lse), _stream(stream))
+
+
+def ring_attn_merge(out_a, lse_a, out_b, lse_b, rows, heads, head_dim, out, lse, stream=None) -> int:
+    return lib().ring_attn_merge(_addr(out_a), _addr(lse_a), _addr(out_b), _addr(lse_b), rows, heads,
+                                 head_dim, _addr(out), _addr(lse), _stream(stream))
+
+
+def ring_attn_bwd(q, k_blocks, v_blocks, out, dout, lse, n_blocks, block_len, heads, kv_heads, head_dim,
+                  causal, rank, dq, dk_blocks, dv_blocks, stream=None) -> int:
+    return lib().ring_attn_bwd(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), _addr(out), _addr(dout),
+                               _addr(lse), n_blocks, block_len, heads, kv_heads, head_dim, int(bool(causal)),
+                               rank, _addr(dq), _ptr_array(dk_blocks), _ptr_array(dv_blocks), _stream(stream))
+
+
+def ring_attn_bwd_f32(q, k_blocks, v_blocks, out, dout, lse, n_blocks, block_len, heads, kv_heads, head_dim,
+                      causal, rank, dq, dk_blocks, dv_blocks, stream=None) -> int:
+    return lib().ring_attn_bwd_f32(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), _addr(out),
+                                   _addr(dout), _addr(lse), n_blocks, block_len, heads, kv_heads, head_dim,
+                                   int(bool(causal)), rank, _addr(dq), _ptr_array(dk_blocks),
+                                   _ptr_array(dv_blocks), _stream(stream))
+
+
+def ring_attn_workspace_bytes(block_len, kv_heads, head_dim, elem_bytes) -> int:
+    return lib().ring_attn_workspace_bytes(block_len, kv_heads, head_dim, elem_bytes)
+
+
+def ring_attn_profile_enable(enable: bool) -> int:
+    return lib().ring_attn_profile_enable(int(bool(enable)))
+
+
+def ring_attn_profile_read():
+    """Returns ({kind: (ms, count)}, copy_ms, hidden_ms) and resets the records."""
+    ms = (ctypes.c_double * 6)()
+    cnt = (ctypes.c_int * 6)()
+    cms, hid = ctypes.c_double(), ctypes.c_double()
+    _check(lib().ring_attn_profile_read(ms, cnt, ctypes.byref(cms), ctypes.byref(hid)))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(PROFILE_KINDS)}, cms.value, hid.value
+
+
+def ring_attn_schedule(rank: int, n_blocks: int, causal: bool) -> List[int]:
+    """Block ids of the rounds one rank executes, in ring order (from the library)."""
+    n = lib().ring_attn_schedule(rank, n_blocks, int(bool(causal)), None, 0)
+    if n < 0:
+        _check(-n)
+    buf = (ctypes.c_int * max(1, n))()
+    m = lib().ring_attn_schedule(rank, n_blocks, int(bool(causal)), buf, n)
+    if m < 0:
+        _check(-m)
+    return list(buf[:m])
+
+
+def ring_attn_debug(poison: bool, delay_cycles: int = 0) -> None:
+    _check(lib().ring_attn_debug(int(bool(poison)), int(delay_cycles)))
+
+
+def ring_attn_shutdown() -> None:
+    lib().ring_attn_shutdown()
+
+
+# ------------------------------------------------------------------ tensor conveniences
+def _dims(q, k0) -> Tuple[int, int, int, int]:
+    block_len, heads, head_dim = q.shape
+    kv_heads = k0.shape[1]
+    return block_len, heads, kv_heads, head_dim
+
+
+def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None, lse=None, stream=None):
+    """Forward ring step on torch tensors; returns (out fp32 [c,Hq,d], lse fp32 [Hq,c])."""
+    import torch
+    c, hq, hkv, d = _dims(q, k_blocks[0])
+    if out is None:
+        out = torch.empty((c, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, c), dtype=torch.float32, device=q.device)
+    fn = ring_attn_fwd if q.dtype == torch.bfloat16 else ring_attn_fwd_f32
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    _check(fn(q, k_blocks, v_blocks, len(k_blocks), c, hq, hkv, d, causal, rank, out, lse, stream))
+    return out, lse
+
+
+def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank: int, dq=None,
+        dk_blocks=None, dv_blocks=None, stream=None):
+    """Backward ring step; dk/dv blocks are accumulated into (zero-initialised if not given)."""
+    import torch
+    c, hq, hkv, d = _dims(q, k_blocks[0])
+    if dq is None:
+        dq = torch.empty((c, hq, d), dtype=torch.float32, device=q.device)
+    if dk_blocks is None:
+        dk_blocks = [torch.zeros((c, hkv, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
+    if dv_blocks is None:
+        dv_blocks = [torch.zeros((c, hkv, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
+    fn = ring_attn_bwd if q.dtype == torch.bfloat16 else ring_attn_bwd_f32
+    _check(fn(q, k_blocks, v_blocks, out, dout, lse, len(k_blocks), c, hq, hkv, d, causal, rank, dq,
+              dk_blocks, dv_blocks, stream))
+    return dq, dk_blocks, dv_blocks
+
+
+def merge(out_a, lse_a, out_b, lse_b, *, out=None, lse=None, stream=None):
+    import torch
+    rows, heads, head_dim = out_a.shape
+    if out is None:
+        out = torch.empty_like(out_a)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    _check(ring_attn_merge(out_a, lse_a, out_b, lse_b, rows, heads, head_dim, out, lse, stream))
+    return out, lse

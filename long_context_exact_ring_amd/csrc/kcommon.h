@@ -1,0 +1,126 @@
+// Device-side building blocks shared by the gfx950 ring-attention kernels.
+//
+// Matrix core: v_mfma_f32_32x32x16_bf16 (bf16 path) and v_mfma_f32_32x32x2_f32
+// (fp32 path).  Both use the same 32x32 fp32 accumulator layout, so one
+// kernel body serves both element types:
+//
+//   A operand (32 rows x 16 k): lane l supplies row l%32, k = (l/32)*8 + e, e=0..7
+//   B operand (16 k x 32 cols): lane l supplies col l%32, k = (l/32)*8 + e
+//   C (32x32 fp32, 16 regs):    lane l holds col l%32, rows (i/4)*8 + (l/32)*4 + i%4
+//
+// A bf16 "fragment" is the 8 k-values of one lane (16 bytes); the fp32 path
+// keeps 8 fp32 values per lane and issues eight k=2 MFMAs, the e-th of which
+// contracts element e of every lane.  Because a contraction may visit its k
+// index in any order, a fragment only has to hold the same logical k values
+// in the A and B operands; the kernels exploit this to feed an accumulator
+// straight back in as the next product's B operand (see key_of_creg).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+typedef uint16_t bf16_storage;  // bf16 values travel as raw 16-bit patterns
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- fragments
+template <typename T> struct Frag;
+template <> struct Frag<bf16_storage> { uint4 v; };
+template <> struct Frag<float> { float4 lo, hi; };
+
+template <typename T> __device__ __forceinline__ Frag<T> frag_zero();
+template <> __device__ __forceinline__ Frag<bf16_storage> frag_zero<bf16_storage>() {
+  return Frag<bf16_storage>{make_uint4(0, 0, 0, 0)};
+}
+template <> __device__ __forceinline__ Frag<float> frag_zero<float>() {
+  return Frag<float>{make_float4(0, 0, 0, 0), make_float4(0, 0, 0, 0)};
+}
+
+// 8 consecutive elements from (global or LDS) memory, 16-byte aligned
+template <typename T> __device__ __forceinline__ Frag<T> frag_load(const T* p);
+template <> __device__ __forceinline__ Frag<bf16_storage> frag_load(const bf16_storage* p) {
+  return Frag<bf16_storage>{*reinterpret_cast<const uint4*>(p)};
+}
+template <> __device__ __forceinline__ Frag<float> frag_load(const float* p) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  return Frag<float>{q[0], q[1]};
+}
+
+// 8 fp32 values -> fragment (bf16: round to nearest even via v_cvt_pk_bf16_f32)
+template <typename T> __device__ __forceinline__ Frag<T> frag_from_f32(const float* x);
+template <> __device__ __forceinline__ Frag<bf16_storage> frag_from_f32(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2_t a = {x[2 * j], x[2 * j + 1]};
+    bf16x2_t b = __builtin_convertvector(a, bf16x2_t);
+    w[j] = __builtin_bit_cast(uint32_t, b);
+  }
+  return Frag<bf16_storage>{make_uint4(w[0], w[1], w[2], w[3])};
+}
+template <> __device__ __forceinline__ Frag<float> frag_from_f32(const float* x) {
+  return Frag<float>{make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7])};
+}
+
+// c += A * B over one 16-wide k slice
+__device__ __forceinline__ void mma(f32x16_t& c, const Frag<bf16_storage>& a,
+                                    const Frag<bf16_storage>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                              __builtin_bit_cast(bf16x8_t, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16_t& c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.x, b.lo.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.y, b.lo.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.z, b.lo.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo.w, b.lo.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.x, b.hi.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.y, b.hi.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.z, b.hi.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi.w, b.hi.w, c, 0, 0, 0);
+}
+
+// Row (within a 32-row C tile) held by accumulator register i of a lane in half hf.
+__device__ __forceinline__ constexpr int crow(int i, int hf) {
+  return ((i >> 2) << 3) + (hf << 2) + (i & 3);
+}
+
+// The accumulator of a 32x32 C tile, read as B operands: registers
+// (kc%2)*8 .. +7 of C tile kc/2 hold rows {crow(i, hf)}, i.e. for 16-row
+// chunk kc the lane in half hf holds rows kc*16 + (e/4)*8 + hf*4 + e%4.
+// The matching A operand must therefore list its k values in that order.
+// perm16(r) gives, for row r of a 16-row chunk, the position at which a
+// lane-contiguous A fragment stores it: half hf = (r/4)%2, element e.
+__device__ __forceinline__ constexpr int perm16(int r) {
+  return (((r >> 2) & 1) << 3) + ((r >> 3) << 2) + (r & 3);
+}
+__device__ __forceinline__ constexpr int perm_pos(int r) {  // any row index
+  return (r & ~15) + perm16(r & 15);
+}
+
+// cross-half exchange: value of lane l ^ 32
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global load / store helpers
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// XCD-aware work order: the dispatcher deals workgroups round-robin over the
+// 8 XCDs, so consecutive logical tiles (which share K/V) are remapped onto
+// one XCD and its L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}
+
+}  // namespace ra

@@ -1,0 +1,75 @@
+// Host-visible launch interface of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ra {
+
+// One forward ring step: queries [len][hq][D] against one K/V block [len][hkv][D].
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;   // [len][hq][D] running output (overwritten when first != 0)
+  float* lse;   // [hq][len] running log-sum-exp (natural log)
+  int len;      // block length (query rows = keys)
+  int hq, hkv;
+  int group;    // hq / hkv
+  int hpw;      // query heads sharing one workgroup (divides group and the wave count)
+  int hsub;     // group / hpw
+  int diag;     // causal diagonal block: key j visible to query i iff j <= i
+  int first;    // first round of the ring: write instead of merge
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+int fwd_waves_per_block();
+
+// Backward: Delta = rowsum(dout * out) per (head, row).
+struct BwdPreArgs {
+  const void* dout;  // [len][hq][D] bf16 or fp32
+  const float* out;  // [len][hq][D]
+  float* delta;      // [hq][len]
+  int len, hq;
+};
+hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+
+// Backward ring step against one K/V block.
+struct BwdArgs {
+  const void* q;     // [len][hq][D]
+  const void* k;     // [len][hkv][D]
+  const void* v;
+  const void* dout;  // [len][hq][D]
+  const float* lse;  // [hq][len]
+  const float* delta;  // [hq][len]
+  float* dq;         // [len][hq][D]   (overwrite when first != 0, else accumulate)
+  float* dk;         // [len][hkv][D]  (accumulate)
+  float* dv;         // [len][hkv][D]  (accumulate)
+  int len, hq, hkv, group;
+  int hpw, hsub;     // dQ kernel: query heads per workgroup (as FwdArgs)
+  int diag;
+  int first;
+  float scale;       // 1/sqrt(D)
+  float scale_log2;  // log2(e)/sqrt(D)
+};
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+int bwd_dq_waves_per_block();
+
+// Pairwise merge of two normalised partials.
+struct MergeArgs {
+  const float* out_a;
+  const float* lse_a;
+  const float* out_b;
+  const float* lse_b;
+  float* out;
+  float* lse;
+  int rows, heads, head_dim;
+};
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+
+// Pipeline diagnostics: NaN-fill two staging buffers; spin for a bounded number of cycles.
+hipError_t launch_fill_nan(void* a, void* b, size_t bytes, hipStream_t st);
+hipError_t launch_spin(long long cycles, hipStream_t st);
+
+}  // namespace ra

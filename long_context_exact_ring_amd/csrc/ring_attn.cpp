@@ -1,0 +1,671 @@
+// Host side of the ring-attention step library: argument validation, the ring
+// schedule, the double-buffered K/V rotation pipeline and the C ABI.
+//
+// Ring schedule (close-reading notes on "Ring Attention with Blockwise
+// Transformers for Near-Infinite Context", §3.2 and the §3.5 walk-through):
+// host r computes in round s with the block it holds, (r - s) mod D, while the
+// block for round s+1 is in flight from the previous host.  On one GPU the
+// "link" is an asynchronous device-to-device copy into one of two staging
+// buffers on a library-owned side stream:
+//
+//   side:  copy(1)->buf1  copy(2)->buf0  [wait done1] copy(3)->buf1  [wait done2] copy(4)->buf0 ...
+//   main:  kernel(0, own block)  [wait copied1] kernel(1, buf1)  [wait copied2] kernel(2, buf0) ...
+//
+// so the copy for round s+1 overlaps the kernel of round s, and a buffer is
+// only refilled after the kernel that read it has finished (the resident
+// "six blocks" of §3.4: Q, O, the K/V in use and the K/V in flight).  With a
+// causal mask the rounds whose block lies in the future are dropped (every
+// rank's own block comes first and is the masked diagonal).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/ring_attn.h"
+#include "kernels.h"
+#include "ring_host.h"
+
+namespace ra {
+
+// ------------------------------------------------------------------ errors
+static thread_local std::string g_last_error;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define RA_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(RA_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));         \
+  } while (0)
+
+// ------------------------------------------------------------------ schedule
+std::vector<int> ring_schedule(int rank, int n_blocks, int causal) {
+  std::vector<int> steps;
+  for (int s = 0; s < n_blocks; ++s) {
+    const int j = ((rank - s) % n_blocks + n_blocks) % n_blocks;
+    if (causal && j > rank) continue;
+    steps.push_back(j);
+  }
+  return steps;
+}
+
+// ------------------------------------------------------------------ validation (no HIP calls)
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int validate_common(const Shape& sh, const void* q, const void* const* kb, const void* const* vb) {
+  if (!q) return fail(RA_ERR_INVALID_ARG, "q is NULL");
+  if (!kb || !vb) return fail(RA_ERR_INVALID_ARG, "k_blocks/v_blocks array is NULL");
+  if (sh.n_blocks < 1) return fail(RA_ERR_INVALID_ARG, "n_blocks must be >= 1 (got %d)", sh.n_blocks);
+  if (sh.rank < 0 || sh.rank >= sh.n_blocks)
+    return fail(RA_ERR_INVALID_ARG, "rank %d outside [0, %d)", sh.rank, sh.n_blocks);
+  if (sh.block_len < 1) return fail(RA_ERR_INVALID_ARG, "block_len must be >= 1 (got %d)", sh.block_len);
+  if (sh.heads < 1 || sh.kv_heads < 1)
+    return fail(RA_ERR_INVALID_ARG, "heads and kv_heads must be >= 1 (got %d, %d)", sh.heads, sh.kv_heads);
+  if (sh.heads % sh.kv_heads != 0)
+    return fail(RA_ERR_INVALID_ARG, "heads (%d) must be a multiple of kv_heads (%d)", sh.heads, sh.kv_heads);
+  if (sh.head_dim != 64 && sh.head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", sh.head_dim);
+  const double elems = (double)sh.block_len * std::max(sh.heads, sh.kv_heads) * sh.head_dim;
+  if (elems >= 2147483647.0)
+    return fail(RA_ERR_INVALID_ARG, "block_len*heads*head_dim = %.0f exceeds 2^31-1", elems);
+  for (int j = 0; j < sh.n_blocks; ++j)
+    if (!kb[j] || !vb[j]) return fail(RA_ERR_INVALID_ARG, "k_blocks[%d] or v_blocks[%d] is NULL", j, j);
+  return RA_OK;
+}
+
+int validate_outputs_disjoint(const Shape& sh, const void* q, const void* const* kb,
+                              const void* const* vb, const void* const* outs, const size_t* out_bytes,
+                              int n_outs, const char* const* names) {
+  const size_t qb = sh.q_bytes(), kvb = sh.kv_bytes();
+  for (int o = 0; o < n_outs; ++o) {
+    if (!outs[o]) return fail(RA_ERR_INVALID_ARG, "%s is NULL", names[o]);
+    if (overlaps(outs[o], out_bytes[o], q, qb)) return fail(RA_ERR_INVALID_ARG, "%s overlaps q", names[o]);
+    for (int j = 0; j < sh.n_blocks; ++j)
+      if (overlaps(outs[o], out_bytes[o], kb[j], kvb) || overlaps(outs[o], out_bytes[o], vb[j], kvb))
+        return fail(RA_ERR_INVALID_ARG, "%s overlaps K/V block %d", names[o], j);
+    for (int p = 0; p < o; ++p)
+      if (overlaps(outs[o], out_bytes[o], outs[p], out_bytes[p]))
+        return fail(RA_ERR_INVALID_ARG, "%s overlaps %s", names[o], names[p]);
+  }
+  return RA_OK;
+}
+
+// ------------------------------------------------------------------ per-device context
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+  int call;
+};
+
+struct Ctx {
+  int device = -1;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_entry = nullptr, ev_side_end = nullptr;
+  hipEvent_t ev_copied[2] = {nullptr, nullptr}, ev_done[2] = {nullptr, nullptr};
+  void* stage = nullptr;  // [kbuf0 | kbuf1 | vbuf0 | vbuf1]
+  size_t stage_cap = 0;
+  float* delta = nullptr;
+  size_t delta_cap = 0;
+};
+
+static std::mutex g_mu;
+static std::vector<Ctx*> g_ctx;
+static bool g_prof = false;
+static std::vector<ProfRec> g_prof_recs;
+static std::vector<hipEvent_t> g_prof_pool;
+static int g_prof_call = 0;
+
+static int get_ctx(Ctx** out) {
+  int dev = 0;
+  RA_HIP(hipGetDevice(&dev));
+  for (Ctx* c : g_ctx)
+    if (c->device == dev) {
+      *out = c;
+      return RA_OK;
+    }
+  Ctx* c = new Ctx();
+  c->device = dev;
+  hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+  hipEvent_t* evs[] = {&c->ev_entry, &c->ev_side_end, &c->ev_copied[0], &c->ev_copied[1], &c->ev_done[0],
+                       &c->ev_done[1]};
+  for (hipEvent_t* ev : evs)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(RA_ERR_HIP, "creating side stream/events: %s", hipGetErrorString(e));
+  }
+  g_ctx.push_back(c);
+  *out = c;
+  return RA_OK;
+}
+
+static int ensure_stage(Ctx* c, size_t bytes) {
+  if (c->stage_cap >= bytes) return RA_OK;
+  if (c->stage) {
+    RA_HIP(hipDeviceSynchronize());
+    RA_HIP(hipFree(c->stage));
+    c->stage = nullptr;
+    c->stage_cap = 0;
+  }
+  if (hipMalloc(&c->stage, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    c->stage = nullptr;
+    return fail(RA_ERR_OOM, "could not allocate %zu bytes of K/V staging", bytes);
+  }
+  c->stage_cap = bytes;
+  return RA_OK;
+}
+
+static int ensure_delta(Ctx* c, size_t bytes) {
+  if (c->delta_cap >= bytes) return RA_OK;
+  if (c->delta) {
+    RA_HIP(hipDeviceSynchronize());
+    RA_HIP(hipFree(c->delta));
+    c->delta = nullptr;
+    c->delta_cap = 0;
+  }
+  if (hipMalloc((void**)&c->delta, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    c->delta = nullptr;
+    return fail(RA_ERR_OOM, "could not allocate %zu bytes for the backward row terms", bytes);
+  }
+  c->delta_cap = bytes;
+  return RA_OK;
+}
+
+// profiling helpers (only active while enabled)
+static hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  int kind;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(int k, hipStream_t s) : kind(k), st(s) {
+    if (g_prof) {
+      a = prof_event();
+      if (a) (void)hipEventRecord(a, st);
+    }
+  }
+  ~ProfScope() {
+    if (a) {
+      hipEvent_t b = prof_event();
+      if (b) {
+        (void)hipEventRecord(b, st);
+        g_prof_recs.push_back(ProfRec{kind, a, b, g_prof_call});
+      }
+    }
+  }
+};
+
+enum { KIND_FWD = 0, KIND_DKDV = 1, KIND_DQ = 2, KIND_PRE = 3, KIND_MERGE = 4, KIND_COPY = 5 };
+
+// ------------------------------------------------------------------ copy engine choice
+static hipMemcpyKind copy_kind() {
+  static int kind = -1;
+  if (kind < 0) {
+    const char* s = getenv("RING_ATTN_COPY");
+    kind = (s && strcmp(s, "kernel") == 0) ? 1 : 0;
+  }
+  return kind == 1 ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToDeviceNoCU;
+}
+
+static int g_poison = 0;
+static long long g_delay_cycles = 0;
+
+static bool log_schedule() {
+  static int v = -1;
+  if (v < 0) {
+    const char* s = getenv("RING_ATTN_LOG");
+    v = (s && s[0] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// ------------------------------------------------------------------ the ring pipeline
+// step_fn(s, j, k_ptr, v_ptr) launches round s's kernels on `stream`.
+template <typename StepFn>
+static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* const* vb,
+                    hipStream_t stream, StepFn&& step_fn) {
+  const std::vector<int> steps = ring_schedule(sh.rank, sh.n_blocks, sh.causal);
+  const int S = (int)steps.size();
+  const size_t kvb = sh.kv_bytes();
+  if (log_schedule()) {
+    fprintf(stderr, "[ring_attn] rank %d/%d causal=%d rounds:", sh.rank, sh.n_blocks, sh.causal);
+    for (int j : steps) fprintf(stderr, " %d", j);
+    fprintf(stderr, "\n");
+  }
+  char* kbuf[2] = {nullptr, nullptr};
+  char* vbuf[2] = {nullptr, nullptr};
+  if (S > 1) {
+    int st = ensure_stage(c, 4 * kvb);
+    if (st != RA_OK) return st;
+    char* base = static_cast<char*>(c->stage);
+    kbuf[0] = base;
+    kbuf[1] = base + kvb;
+    vbuf[0] = base + 2 * kvb;
+    vbuf[1] = base + 3 * kvb;
+    RA_HIP(hipEventRecord(c->ev_entry, stream));
+    RA_HIP(hipStreamWaitEvent(c->side, c->ev_entry, 0));
+  }
+  auto issue_copy = [&](int s) -> int {
+    const int b = s & 1, j = steps[s];
+    if (g_poison && s >= 3) RA_HIP(launch_fill_nan(kbuf[b], vbuf[b], kvb, c->side));
+    if (g_delay_cycles > 0) RA_HIP(launch_spin(g_delay_cycles, c->side));
+    {
+      ProfScope ps(KIND_COPY, c->side);
+      RA_HIP(hipMemcpyAsync(kbuf[b], kb[j], kvb, copy_kind(), c->side));
+      RA_HIP(hipMemcpyAsync(vbuf[b], vb[j], kvb, copy_kind(), c->side));
+    }
+    RA_HIP(hipEventRecord(c->ev_copied[b], c->side));
+    return RA_OK;
+  };
+  int st;
+  if (S > 1 && (st = issue_copy(1)) != RA_OK) return st;
+  if (S > 2 && (st = issue_copy(2)) != RA_OK) return st;
+  if ((st = step_fn(0, steps[0], kb[steps[0]], vb[steps[0]])) != RA_OK) return st;
+  for (int s = 1; s < S; ++s) {
+    const int b = s & 1;
+    RA_HIP(hipStreamWaitEvent(stream, c->ev_copied[b], 0));
+    if ((st = step_fn(s, steps[s], kbuf[b], vbuf[b])) != RA_OK) return st;
+    if (s + 2 < S) {
+      RA_HIP(hipEventRecord(c->ev_done[b], stream));
+      RA_HIP(hipStreamWaitEvent(c->side, c->ev_done[b], 0));
+      if ((st = issue_copy(s + 2)) != RA_OK) return st;
+    }
+  }
+  if (S > 1) {
+    RA_HIP(hipEventRecord(c->ev_side_end, c->side));
+    RA_HIP(hipStreamWaitEvent(stream, c->ev_side_end, 0));
+  }
+  return RA_OK;
+}
+
+static float rsqrt_dim(int d) { return 1.0f / std::sqrt((float)d); }
+
+// Query heads that share one workgroup: the largest common divisor of the group
+// size and the wave count (each wave owns 32 rows of one head).
+static int heads_per_block(int group, int waves) {
+  for (int x = waves; x >= 1; --x)
+    if (group % x == 0 && waves % x == 0) return x;
+  return 1;
+}
+
+int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const Shape& sh, float* out,
+             float* lse, hipStream_t stream) {
+  int st = validate_common(sh, q, kb, vb);
+  if (st != RA_OK) return st;
+  const void* outs[] = {out, lse};
+  const size_t ob[] = {sh.out_bytes(), sh.lse_bytes()};
+  const char* names[] = {"out", "lse"};
+  if ((st = validate_outputs_disjoint(sh, q, kb, vb, outs, ob, 2, names)) != RA_OK) return st;
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  Ctx* c = nullptr;
+  if ((st = get_ctx(&c)) != RA_OK) return st;
+  ++g_prof_call;
+  const int group = sh.heads / sh.kv_heads;
+  const int hpw = heads_per_block(group, fwd_waves_per_block());
+  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
+    FwdArgs a{};
+    a.q = q;
+    a.k = kp;
+    a.v = vp;
+    a.out = out;
+    a.lse = lse;
+    a.len = sh.block_len;
+    a.hq = sh.heads;
+    a.hkv = sh.kv_heads;
+    a.group = group;
+    a.hpw = hpw;
+    a.hsub = group / hpw;
+    a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
+    a.first = (s == 0) ? 1 : 0;
+    a.scale_log2 = 1.4426950408889634f * rsqrt_dim(sh.head_dim);
+    ProfScope ps(KIND_FWD, stream);
+    RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
+    return RA_OK;
+  };
+  return run_ring(c, sh, kb, vb, stream, step);
+}
+
+int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const float* out,
+             const void* dout, const float* lse, const Shape& sh, float* dq, float* const* dkb,
+             float* const* dvb, hipStream_t stream) {
+  int st = validate_common(sh, q, kb, vb);
+  if (st != RA_OK) return st;
+  if (!out || !dout || !lse) return fail(RA_ERR_INVALID_ARG, "out, dout or lse is NULL");
+  if (!dkb || !dvb) return fail(RA_ERR_INVALID_ARG, "dk_blocks/dv_blocks array is NULL");
+  std::vector<const void*> outs;
+  std::vector<size_t> ob;
+  std::vector<std::string> nm;
+  outs.push_back(dq);
+  ob.push_back(sh.out_bytes());
+  nm.push_back("dq");
+  for (int j = 0; j < sh.n_blocks; ++j) {
+    outs.push_back(dkb[j]);
+    ob.push_back(sh.kv_f32_bytes());
+    nm.push_back("dk_blocks[" + std::to_string(j) + "]");
+    outs.push_back(dvb[j]);
+    ob.push_back(sh.kv_f32_bytes());
+    nm.push_back("dv_blocks[" + std::to_string(j) + "]");
+  }
+  // gradients must also stay clear of the other read-only inputs
+  const void* ro[] = {out, dout, lse};
+  const size_t rob[] = {sh.out_bytes(), sh.q_bytes(), sh.lse_bytes()};
+  std::vector<const char*> names;
+  for (auto& s : nm) names.push_back(s.c_str());
+  if ((st = validate_outputs_disjoint(sh, q, kb, vb, outs.data(), ob.data(), (int)outs.size(),
+                                      names.data())) != RA_OK)
+    return st;
+  for (size_t o = 0; o < outs.size(); ++o)
+    for (int r = 0; r < 3; ++r)
+      if (overlaps(outs[o], ob[o], ro[r], rob[r]))
+        return fail(RA_ERR_INVALID_ARG, "%s overlaps a forward input (out/dout/lse)", names[o]);
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  Ctx* c = nullptr;
+  if ((st = get_ctx(&c)) != RA_OK) return st;
+  ++g_prof_call;
+  if ((st = ensure_delta(c, sh.lse_bytes())) != RA_OK) return st;
+  {
+    BwdPreArgs p{dout, out, c->delta, sh.block_len, sh.heads};
+    ProfScope ps(KIND_PRE, stream);
+    RA_HIP(launch_bwd_pre(p, sh.elem_bytes, sh.head_dim, stream));
+  }
+  const float scale = rsqrt_dim(sh.head_dim);
+  const int group = sh.heads / sh.kv_heads;
+  const int hpw = heads_per_block(group, bwd_dq_waves_per_block());
+  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
+    BwdArgs a{};
+    a.q = q;
+    a.k = kp;
+    a.v = vp;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = c->delta;
+    a.dq = dq;
+    a.dk = dkb[j];
+    a.dv = dvb[j];
+    a.len = sh.block_len;
+    a.hq = sh.heads;
+    a.hkv = sh.kv_heads;
+    a.group = group;
+    a.hpw = hpw;
+    a.hsub = group / hpw;
+    a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
+    a.first = (s == 0) ? 1 : 0;
+    a.scale = scale;
+    a.scale_log2 = 1.4426950408889634f * scale;
+    {
+      ProfScope ps(KIND_DKDV, stream);
+      RA_HIP(launch_bwd_dkdv(a, sh.elem_bytes, sh.head_dim, stream));
+    }
+    {
+      ProfScope ps(KIND_DQ, stream);
+      RA_HIP(launch_bwd_dq(a, sh.elem_bytes, sh.head_dim, stream));
+    }
+    return RA_OK;
+  };
+  return run_ring(c, sh, kb, vb, stream, step);
+}
+
+int merge_impl(const float* oa, const float* la, const float* obp, const float* lb, int rows, int heads,
+               int head_dim, float* out, float* lse, hipStream_t stream) {
+  if (!oa || !la || !obp || !lb || !out || !lse)
+    return fail(RA_ERR_INVALID_ARG, "merge: NULL pointer argument");
+  if (rows < 0 || heads < 1 || head_dim < 1)
+    return fail(RA_ERR_INVALID_ARG, "merge: bad sizes rows=%d heads=%d head_dim=%d", rows, heads, head_dim);
+  if ((double)rows * heads * head_dim >= 2147483647.0)
+    return fail(RA_ERR_INVALID_ARG, "merge: rows*heads*head_dim exceeds 2^31-1");
+  const size_t obytes = (size_t)rows * heads * head_dim * 4, lbytes = (size_t)rows * heads * 4;
+  // exact aliasing with an input is the supported in-place form; partial overlap is not
+  const void* ins_o[] = {oa, obp};
+  const void* ins_l[] = {la, lb};
+  for (int i = 0; i < 2; ++i) {
+    if (out != ins_o[i] && overlaps(out, obytes, ins_o[i], obytes))
+      return fail(RA_ERR_INVALID_ARG, "merge: out partially overlaps an input");
+    if (lse != ins_l[i] && overlaps(lse, lbytes, ins_l[i], lbytes))
+      return fail(RA_ERR_INVALID_ARG, "merge: lse partially overlaps an input");
+    if (overlaps(out, obytes, ins_l[i], lbytes) || overlaps(lse, lbytes, ins_o[i], obytes))
+      return fail(RA_ERR_INVALID_ARG, "merge: out/lse overlap the other kind of input");
+  }
+  if (overlaps(out, obytes, lse, lbytes)) return fail(RA_ERR_INVALID_ARG, "merge: out overlaps lse");
+  if (rows == 0) return RA_OK;
+  std::lock_guard<std::mutex> lk(g_mu);
+  ++g_prof_call;
+  MergeArgs a{oa, la, obp, lb, out, lse, rows, heads, head_dim};
+  ProfScope ps(KIND_MERGE, stream);
+  RA_HIP(launch_merge(a, stream));
+  return RA_OK;
+}
+
+// ------------------------------------------------------------------ profiling readout
+int debug_set(int poison, long long delay_cycles) {
+  if (delay_cycles < 0) return fail(RA_ERR_INVALID_ARG, "delay_cycles must be >= 0");
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_poison = poison != 0;
+  g_delay_cycles = delay_cycles;
+  return RA_OK;
+}
+
+int profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_prof = on != 0;
+  return RA_OK;
+}
+
+int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
+  if (!ms || !count) return fail(RA_ERR_INVALID_ARG, "profile_read: NULL output array");
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (int k = 0; k < 6; ++k) {
+    ms[k] = 0.0;
+    count[k] = 0;
+  }
+  double cms = 0.0, hid = 0.0;
+  if (!g_prof_recs.empty()) {
+    hipEvent_t ref = g_prof_recs.front().a;
+    for (auto& r : g_prof_recs) RA_HIP(hipEventSynchronize(r.b));
+    struct Iv {
+      double a, b;
+      int call;
+    };
+    std::vector<Iv> kern, copy;
+    for (auto& r : g_prof_recs) {
+      float ta = 0.f, tb = 0.f;
+      RA_HIP(hipEventElapsedTime(&ta, ref, r.a));
+      RA_HIP(hipEventElapsedTime(&tb, ref, r.b));
+      ms[r.kind] += tb - ta;
+      count[r.kind] += 1;
+      if (r.kind == KIND_COPY) copy.push_back({ta, tb, r.call});
+      else kern.push_back({ta, tb, r.call});
+    }
+    for (auto& cp : copy) {
+      cms += cp.b - cp.a;
+      // overlap of this copy with the union of kernel intervals
+      std::vector<std::pair<double, double>> cut;
+      for (auto& k : kern) {
+        const double lo = std::max(cp.a, k.a), hi = std::min(cp.b, k.b);
+        if (hi > lo) cut.push_back({lo, hi});
+      }
+      std::sort(cut.begin(), cut.end());
+      double cur_lo = -1e300, cur_hi = -1e300;
+      for (auto& iv : cut) {
+        if (iv.first > cur_hi) {
+          if (cur_hi > cur_lo) hid += cur_hi - cur_lo;
+          cur_lo = iv.first;
+          cur_hi = iv.second;
+        } else {
+          cur_hi = std::max(cur_hi, iv.second);
+        }
+      }
+      if (cur_hi > cur_lo) hid += cur_hi - cur_lo;
+    }
+    for (auto& r : g_prof_recs) {
+      g_prof_pool.push_back(r.a);
+      g_prof_pool.push_back(r.b);
+    }
+    g_prof_recs.clear();
+  }
+  if (copy_ms) *copy_ms = cms;
+  if (hidden_ms) *hidden_ms = hid;
+  return RA_OK;
+}
+
+void shutdown_all() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_ctx.empty()) (void)hipDeviceSynchronize();
+  for (Ctx* c : g_ctx) {
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    if (c->stage) (void)hipFree(c->stage);
+    if (c->delta) (void)hipFree(c->delta);
+    hipEvent_t evs[] = {c->ev_entry, c->ev_side_end, c->ev_copied[0], c->ev_copied[1], c->ev_done[0],
+                        c->ev_done[1]};
+    for (hipEvent_t e : evs)
+      if (e) (void)hipEventDestroy(e);
+    if (c->side) (void)hipStreamDestroy(c->side);
+    (void)hipSetDevice(prev);
+    delete c;
+  }
+  g_ctx.clear();
+  for (auto& r : g_prof_recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof_recs.clear();
+  for (hipEvent_t e : g_prof_pool) (void)hipEventDestroy(e);
+  g_prof_pool.clear();
+}
+
+const char* last_error() { return g_last_error.c_str(); }
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace ra
+
+// ====================================================================== C ABI
+extern "C" {
+
+static ra::Shape make_shape(int n_blocks, int block_len, int heads, int kv_heads, int head_dim, int causal,
+                            int rank, int elem_bytes) {
+  ra::Shape s;
+  s.n_blocks = n_blocks;
+  s.block_len = block_len;
+  s.heads = heads;
+  s.kv_heads = kv_heads;
+  s.head_dim = head_dim;
+  s.causal = causal ? 1 : 0;
+  s.rank = rank;
+  s.elem_bytes = elem_bytes;
+  return s;
+}
+
+int ring_attn_fwd(const void* q, const void* const* k_blocks, const void* const* v_blocks, int n_blocks,
+                  int block_len, int heads, int kv_heads, int head_dim, int causal, int rank, float* out,
+                  float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::fwd_impl(q, k_blocks, v_blocks,
+                      make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 2), out, lse,
+                      (hipStream_t)stream);
+}
+
+int ring_attn_fwd_f32(const float* q, const float* const* k_blocks, const float* const* v_blocks,
+                      int n_blocks, int block_len, int heads, int kv_heads, int head_dim, int causal, int rank,
+                      float* out, float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::fwd_impl(q, (const void* const*)k_blocks, (const void* const*)v_blocks,
+                      make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 4), out, lse,
+                      (hipStream_t)stream);
+}
+
+int ring_attn_merge(const float* out_a, const float* lse_a, const float* out_b, const float* lse_b, int rows,
+                    int heads, int head_dim, float* out, float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::merge_impl(out_a, lse_a, out_b, lse_b, rows, heads, head_dim, out, lse, (hipStream_t)stream);
+}
+
+int ring_attn_bwd(const void* q, const void* const* k_blocks, const void* const* v_blocks, const float* out,
+                  const void* dout, const float* lse, int n_blocks, int block_len, int heads, int kv_heads,
+                  int head_dim, int causal, int rank, float* dq, float* const* dk_blocks,
+                  float* const* dv_blocks, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::bwd_impl(q, k_blocks, v_blocks, out, dout, lse,
+                      make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 2), dq,
+                      dk_blocks, dv_blocks, (hipStream_t)stream);
+}
+
+int ring_attn_bwd_f32(const float* q, const float* const* k_blocks, const float* const* v_blocks,
+                      const float* out, const float* dout, const float* lse, int n_blocks, int block_len,
+                      int heads, int kv_heads, int head_dim, int causal, int rank, float* dq,
+                      float* const* dk_blocks, float* const* dv_blocks, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::bwd_impl(q, (const void* const*)k_blocks, (const void* const*)v_blocks, out, dout, lse,
+                      make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 4), dq,
+                      dk_blocks, dv_blocks, (hipStream_t)stream);
+}
+
+int ring_attn_schedule(int rank, int n_blocks, int causal, int* steps, int max_steps) {
+  ra::clear_error();
+  if (n_blocks < 1 || rank < 0 || rank >= n_blocks)
+    return -ra::fail(RA_ERR_INVALID_ARG, "schedule: rank %d / n_blocks %d invalid", rank, n_blocks);
+  const std::vector<int> s = ra::ring_schedule(rank, n_blocks, causal);
+  if (steps) {
+    if (max_steps < (int)s.size())
+      return -ra::fail(RA_ERR_INVALID_ARG, "schedule: steps holds %d < %d entries", max_steps, (int)s.size());
+    for (size_t i = 0; i < s.size(); ++i) steps[i] = s[i];
+  }
+  return (int)s.size();
+}
+
+int ring_attn_debug(int poison, long long delay_cycles) {
+  ra::clear_error();
+  return ra::debug_set(poison, delay_cycles);
+}
+
+const char* ring_attn_last_error(void) { return ra::last_error(); }
+
+size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int elem_bytes) {
+  if (block_len < 1 || kv_heads < 1 || head_dim < 1 || (elem_bytes != 2 && elem_bytes != 4)) return 0;
+  return 4 * (size_t)block_len * kv_heads * head_dim * elem_bytes;
+}
+
+int ring_attn_profile_enable(int enable) { return ra::profile_enable(enable); }
+
+int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
+  ra::clear_error();
+  return ra::profile_read(ms, count, copy_ms, hidden_ms);
+}
+
+void ring_attn_shutdown(void) { ra::shutdown_all(); }
+
+}  // extern "C"
