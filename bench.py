@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring-attention step on one MI355X.
+
+One "step" is one pass of the whole hot path over the workload's synthetic
+input: for every rank of the workload, the forward ring step (schedule,
+double-buffered K/V rotation copies, QK^T / online softmax / PV, merge into
+the running output) and, if the workload has a backward, the backward ring
+step of every rank (row terms, dK/dV and dQ kernels, the same rotation).
+
+Prints ONE JSON line.  ``value`` is the algorithmic TFLOP/s of the whole step
+(forward 4*d*Hq per visible query/key pair, backward 2.5x that), with inputs
+resident in HBM before the timed region.  Per-kernel averages come from HIP
+events the library records around its own launches during the timed region.
+
+Only one GPU is supported: ``--gpus N`` with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ring-attn fwd/bwd TFLOP/s on 1 MI355X + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", default="causal_128k_h32_d128")
+    p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48, help="query rows in the CPU oracle sample")
+    return p.parse_args()
+
+
+def build_inputs(w, torch):
+    """Seeded synthetic blocks, uploaded once (outside the timed region)."""
+    from workloads import bf16_bits, gen_block
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(bf16_bits(x).view("int16")).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    c = w.block_len
+    t0 = time.time()
+    kb = [up(gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype)) for j in range(w.n_blocks)]
+    vb = [up(gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype)) for j in range(w.n_blocks)]
+    qs = {r: up(gen_block(w.seed, "q", r, c, w.heads, w.head_dim, w.dtype)) for r in w.ranks}
+    dos = {}
+    if w.backward:
+        dos = {r: up(gen_block(w.seed, "do", r, c, w.heads, w.head_dim, w.dtype)) for r in w.ranks}
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated and uploaded in {time.time() - t0:.1f}s (dtype {tdt})")
+    return qs, kb, vb, dos
+
+
+def cpu_baseline(w, rows: int):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from workloads import gen_block
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    r = max(w.ranks)
+    c = w.block_len
+    nblk = r + 1 if w.causal else w.n_blocks
+    k = np.concatenate([gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(nblk)])
+    v = np.concatenate([gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(nblk)])
+    q = gen_block(w.seed, "q", r, c, w.heads, w.head_dim, w.dtype)
+    sel = np.linspace(0, c - 1, rows).astype(np.int64)
+    qpos = r * c + sel
+    t0 = time.time()
+    if w.backward:
+        do = gen_block(w.seed, "do", r, c, w.heads, w.head_dim, w.dtype)
+        oracle.attention_bwd(q[sel], k, v, do[sel], causal=w.causal, q_pos=qpos)
+    else:
+        oracle.attention_fwd(q[sel], k, v, causal=w.causal, q_pos=qpos)
+    dt = time.time() - t0
+    pairs = float(np.sum(qpos + 1)) if w.causal else float(rows * w.seq_len)
+    flop = 4.0 * w.head_dim * w.heads * pairs * (3.5 if w.backward else 1.0)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, {'forward+backward' if w.backward else 'forward'} of {rows} "
+                       f"evenly spaced query rows x {w.heads} heads of rank {r} against its "
+                       f"{k.shape[0]} visible keys ({dt:.1f}s)"),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
+              f"in this library", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import long_context_exact_ring_amd as ra
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    do_bwd = w.backward and not args.fwd_only
+    torch.cuda.set_device(0)
+    qs, kb, vb, dos = build_inputs(w, torch)
+    c, hq, hkv, d = w.block_len, w.heads, w.kv_heads, w.head_dim
+    outs = {r: torch.empty((c, hq, d), dtype=torch.float32, device="cuda") for r in w.ranks}
+    lses = {r: torch.empty((hq, c), dtype=torch.float32, device="cuda") for r in w.ranks}
+    if do_bwd:
+        dqs = {r: torch.empty((c, hq, d), dtype=torch.float32, device="cuda") for r in w.ranks}
+        dkb = [torch.zeros((c, hkv, d), dtype=torch.float32, device="cuda") for _ in range(w.n_blocks)]
+        dvb = [torch.zeros((c, hkv, d), dtype=torch.float32, device="cuda") for _ in range(w.n_blocks)]
+
+    def step():
+        for r in w.ranks:
+            ra.fwd(qs[r], kb, vb, causal=w.causal, rank=r, out=outs[r], lse=lses[r])
+        if do_bwd:
+            for t in dkb + dvb:
+                t.zero_()
+            for r in w.ranks:
+                ra.bwd(qs[r], kb, vb, outs[r], dos[r], lses[r], causal=w.causal, rank=r, dq=dqs[r],
+                       dk_blocks=dkb, dv_blocks=dvb)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup step(s) done")
+
+    ra.ring_attn_profile_enable(True)
+    ra.ring_attn_profile_read()  # discard anything recorded before
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    recs, copy_ms, hidden_ms = ra.ring_attn_profile_read()
+    ra.ring_attn_profile_enable(False)
+    ms_step = ms_total / args.steps
+    log(f"[bench] {args.steps} timed step(s): {ms_step:.3f} ms/step")
+
+    fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if do_bwd else 0.0)
+    step_flop = fwd_flop + bwd_flop
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    # per-kernel averages over the timed region (library HIP events on the launch stream)
+    kern = {}
+    alg = {"fwd_step": fwd_flop, "bwd_dkdv": 0.8 * bwd_flop, "bwd_dq": 0.2 * bwd_flop}
+    for name, (ms, cnt) in recs.items():
+        if cnt:
+            per = ms / args.steps
+            kern[name] = {"launches_per_step": cnt // args.steps, "avg_launch_ms": ms / cnt,
+                          "ms_per_step": per}
+            if name in alg and alg[name] > 0:
+                kern[name]["achieved_tflops"] = alg[name] / (per * 1e-3) / 1e12
+    mm = [(v["ms_per_step"], k) for k, v in kern.items() if k in alg and alg[k] > 0]
+    dom = max(mm)[1] if mm else "fwd_step"
+    dom_ms = kern.get(dom, {}).get("ms_per_step", float("nan"))
+    achieved = alg[dom] / (dom_ms * 1e-3) / 1e12 if dom in kern else None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": (achieved / peak) if achieved else None, "traffic": None}
+
+    overlap = {"copy_ms_per_step": copy_ms / args.steps, "hidden_ms_per_step": hidden_ms / args.steps,
+               "hidden_frac": (hidden_ms / copy_ms) if copy_ms > 0 else None,
+               "copy_engine": os.environ.get("RING_ATTN_COPY", "sdma")}
+
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": w.seq_len, "n_blocks": w.n_blocks, "block_len": c,
+                   "heads": hq, "kv_heads": hkv, "head_dim": d, "causal": w.causal,
+                   "ranks": len(w.ranks), "pass": "forward+backward" if do_bwd else "forward",
+                   "batch": 1},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "fwd_tflops": None, "bwd_tflops": None,
+        "kernels": kern, "overlap": overlap, "roofline": roofline,
+    }
+    if "fwd_step" in kern:
+        # forward-only rate over the forward kernels' own time
+        result["fwd_tflops"] = round(fwd_flop / (kern["fwd_step"]["ms_per_step"] * 1e-3) / 1e12, 2)
+    if do_bwd and "bwd_dkdv" in kern:
+        bms = sum(kern[k]["ms_per_step"] for k in ("bwd_dkdv", "bwd_dq", "bwd_pre") if k in kern)
+        result["bwd_tflops"] = round(bwd_flop / (bms * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
