@@ -325,14 +325,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-constexpr int kBwdWaves = 4;
+#ifndef RA_DQ_WAVES
+#define RA_DQ_WAVES 8
+#endif
+#ifndef RA_KV_WAVES
+#define RA_KV_WAVES 8
+#endif
+#ifndef RA_DQ_BC
+#define RA_DQ_BC 64
+#endif
+#ifndef RA_KV_BR
+#define RA_KV_BR 32
+#endif
+constexpr int kBwdWaves = RA_DQ_WAVES;
+constexpr int kKvWaves = RA_KV_WAVES;
 
 template <typename T, int D, int BR>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
-  const int KW = kBwdWaves * 32;
+  const int KW = kKvWaves * 32;
   const int nblk = ((a.len + KW - 1) / KW) * a.hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BR, kBwdWaves>), dim3(nblk), dim3(kBwdWaves * 64), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BR, kKvWaves>), dim3(nblk), dim3(kKvWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -349,7 +362,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dkdv_t<bf16_storage, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dkdv_t<bf16_storage, 128, 32>(a, st);
+    if (head_dim == 128) return launch_dkdv_t<bf16_storage, 128, RA_KV_BR>(a, st);
   } else {
     if (head_dim == 64) return launch_dkdv_t<float, 64, 32>(a, st);
     if (head_dim == 128) return launch_dkdv_t<float, 128, 32>(a, st);
@@ -360,7 +373,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipSt
 hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dq_t<bf16_storage, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dq_t<bf16_storage, 128, 32>(a, st);
+    if (head_dim == 128) return launch_dq_t<bf16_storage, 128, RA_DQ_BC>(a, st);
   } else {
     if (head_dim == 64) return launch_dq_t<float, 64, 32>(a, st);
     if (head_dim == 128) return launch_dq_t<float, 128, 32>(a, st);

@@ -29,6 +29,7 @@
 //    (out, lse) in HBM.
 #include "kcommon.h"
 #include "kernels.h"
+#include "tile_stage.h"
 
 namespace ra {
 
@@ -43,17 +44,79 @@ struct FwdCfg {
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int LDS = 2 * STAGE;
-  static constexpr int KCH = BC * (D / CH);     // 16-byte K chunks per tile
-  static constexpr int KIT = KCH / NT;
-  static constexpr int VCH = (BC / 2) * (D / CH);  // (key pair, 16-byte chunk) items per tile
-  static constexpr int VIT = VCH / NT;
-  static_assert(KCH % NT == 0 && VCH % NT == 0, "tile not divisible among threads");
-  static_assert((D / CH) % 4 == 0, "V staging groups 4 chunks");
   static_assert(BC % 32 == 0 && D % 32 == 0, "32x32 MFMA tiles");
 };
 
+// Normalise this lane's query row and write it, or merge it into the running
+// (out, lse) of earlier rounds: lse' = log(e^lse + e^lse_blk),
+// out' = e^(lse - lse') out + e^(lse_blk - lse') O_blk.  m_run is the reference
+// max (log2 units) the block's exponentials were taken against; l_run is this
+// lane's half of the row sum (the other half sits in lane ^ 32).
+template <int D>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16_t (&o)[D / 32], float m_run,
+                                             float l_run, int head, int qi, int hf) {
+  const float l_tot = l_run + swap_halves(l_run);
+  if (qi >= a.len) return;
+  const size_t qstride = (size_t)a.hq * D;
+  float* orow = a.out + (size_t)qi * qstride + (size_t)head * D;
+  float* lsep = a.lse + (size_t)head * a.len + qi;
+  float lse_cur, w_cur, w_old = 0.f;
+  if (l_tot > 0.f) {
+    lse_cur = (m_run + log2f(l_tot)) * kLn2;
+    w_cur = 1.f / l_tot;
+  } else {
+    lse_cur = kNegInf;
+    w_cur = 0.f;
+  }
+  float lse_new = lse_cur;
+  if (!a.first) {
+    const float lse_old = *lsep;
+    const float mxl = fmaxf(lse_old, lse_cur);
+    if (mxl == kNegInf) {
+      lse_new = kNegInf;
+      w_old = 0.f;
+      w_cur = 0.f;
+    } else {
+      const float eo = expf(lse_old - mxl), ec = expf(lse_cur - mxl);
+      const float z = eo + ec;
+      lse_new = mxl + logf(z);
+      w_old = eo / z;
+      w_cur *= ec / z;
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4* dst = reinterpret_cast<float4*>(orow + dt * 32 + j * 8 + hf * 4);
+      float4 r = make_float4(o[dt][4 * j] * w_cur, o[dt][4 * j + 1] * w_cur, o[dt][4 * j + 2] * w_cur,
+                             o[dt][4 * j + 3] * w_cur);
+      if (!a.first) {
+        const float4 old = *dst;
+        r.x += w_old * old.x;
+        r.y += w_old * old.y;
+        r.z += w_old * old.z;
+        r.w += w_old * old.w;
+      }
+      *dst = r;
+    }
+  if (hf == 0) *lsep = lse_new;
+}
+
+#ifndef RA_FWD_WAVES
+#define RA_FWD_WAVES 8
+#endif
+#ifndef RA_FWD_BC
+#define RA_FWD_BC 64
+#endif
+#ifdef RA_FWD_WPE
+#define RA_FWD_OCC __attribute__((amdgpu_waves_per_eu(RA_FWD_WPE)))
+#else
+#define RA_FWD_OCC
+#endif
+
 template <typename T, int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_step_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a) {
   using C = FwdCfg<T, D, BC, NW>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
 
@@ -92,59 +155,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_step_kernel(FwdArgs a) {
       qf[ks] = (qrow < a.len) ? frag_load<T>(qp + ks * 16) : frag_zero<T>();
   }
 
-  // ------------------------------------------------ K/V staging
-  uint4 kreg[C::KIT];
-  uint4 vreg[C::VIT][2];
+  // ------------------------------------------------ K/V staging (natural K, permuted V^T)
+  using St = TileStager<T, BC, D, C::NT>;
+  static_assert(St::NROW == C::KROW && St::TROW == C::VROW, "LDS pitches");
+  St kst, vst;
   auto gload = [&](int t0) {
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int id = it * C::NT + tid;
-      const int r = id / (D / C::CH), ch = id % (D / C::CH);
-      const int key = t0 + r;
-      kreg[it] = (key < a.len) ? ld16(kbase + (size_t)key * kvstride + ch * C::CH) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int id = it * C::NT + tid;
-      const int dc = ((id >> 2) / (BC / 2)) * 4 + (id & 3);
-      const int kp = (id >> 2) % (BC / 2);
-      const int key = t0 + 2 * kp;
-      const T* p = vbase + (size_t)key * kvstride + dc * C::CH;
-      vreg[it][0] = (key < a.len) ? ld16(p) : make_uint4(0, 0, 0, 0);
-      vreg[it][1] = (key + 1 < a.len) ? ld16(p + kvstride) : make_uint4(0, 0, 0, 0);
-    }
+    kst.load(kbase, kvstride, t0, a.len, tid);
+    vst.load(vbase, kvstride, t0, a.len, tid);
   };
   auto lstore = [&](int buf) {
     unsigned char* ks = smem + buf * C::STAGE;
-    unsigned char* vs = ks + C::KBYTES;
-#pragma unroll
-    for (int it = 0; it < C::KIT; ++it) {
-      const int id = it * C::NT + tid;
-      const int r = id / (D / C::CH), ch = id % (D / C::CH);
-      st16(ks + r * C::KROW + ch * 16, kreg[it]);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VIT; ++it) {
-      const int id = it * C::NT + tid;
-      const int dc = ((id >> 2) / (BC / 2)) * 4 + (id & 3);
-      const int kp = (id >> 2) % (BC / 2);
-      const int pos = perm_pos(2 * kp);  // keys 2kp, 2kp+1 stay adjacent
-      const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vreg[it][0]);
-      const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vreg[it][1]);
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t lo = (a0[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          const uint32_t hi = (a1[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-          *reinterpret_cast<uint32_t*>(vs + (dc * 8 + e) * C::VROW + pos * 2) = lo | (hi << 16);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<uint2*>(vs + (dc * 4 + e) * C::VROW + pos * 4) = make_uint2(a0[e], a1[e]);
-        }
-      }
-    }
+    kst.store(ks, nullptr, tid);
+    vst.store(nullptr, ks + C::KBYTES, tid);
   };
 
   // ------------------------------------------------ running state (one query per lane)
@@ -232,53 +254,241 @@ __global__ __launch_bounds__(NW * 64) void fwd_step_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  // ------------------------------------------------ epilogue: normalise and merge
-  const int qi = row0 + n;
-  if (qi >= a.len) return;
-  const float l_tot = l_run + swap_halves(l_run);
-  float* orow = a.out + (size_t)qi * qstride + (size_t)head * D;
-  float* lsep = a.lse + (size_t)head * a.len + qi;
-  float lse_cur, w_cur, w_old = 0.f;
-  if (l_tot > 0.f) {
-    lse_cur = (m_run + log2f(l_tot)) * kLn2;
-    w_cur = 1.f / l_tot;
-  } else {
-    lse_cur = kNegInf;
-    w_cur = 0.f;
-  }
-  float lse_new = lse_cur;
-  if (!a.first) {
-    const float lse_old = *lsep;
-    const float mxl = fmaxf(lse_old, lse_cur);
-    if (mxl == kNegInf) {
-      lse_new = kNegInf;
-      w_old = 0.f;
-      w_cur = 0.f;
-    } else {
-      const float eo = expf(lse_old - mxl), ec = expf(lse_cur - mxl);
-      const float z = eo + ec;
-      lse_new = mxl + logf(z);
-      w_old = eo / z;
-      w_cur *= ec / z;
+  fwd_epilogue<D>(a, o, m_run, l_run, head, row0 + n, hf);
+}
+
+
+// ============================================================================
+// bf16 path.  Same mathematics as fwd_step_kernel, arranged for the VALU
+// budget of gfx950 (the softmax instructions, not the MFMAs, set the pace):
+//  * K and V tiles are copied global -> LDS by the load unit itself
+//    (global_load_lds_dwordx4: no staging registers, no VALU), 1 KB per wave
+//    instruction, rows unpadded with an XOR swizzle of the 16-byte chunks so
+//    that the MFMA operand reads are bank-conflict free.
+//  * V stays in its natural [key][d] layout; the transposed A operand of
+//    O^T += V^T P^T is read with ds_read_b64_tr_b16 (four keys of one column
+//    per read), keys ordered to match the accumulator-fed P^T fragments.
+//  * The hot path carries no masking; diagonal / ragged tiles take a separate
+//    instantiation.
+//  * Lazy rescaling: the running max used as exponent reference only moves
+//    when a row's new max exceeds it by more than 2^8 (probabilities stay
+//    below 256, far from fp32/bf16 range limits), so the O rescale is skipped
+//    on almost every tile.  Results are exact either way: the reference max
+//    cancels in the final normalisation.
+// ============================================================================
+template <int D> struct Swz;
+template <> struct Swz<128> {  // 256-byte rows: one row spans all 64 banks
+  __device__ static constexpr int k(int r) { return r & 15; }
+  __device__ static constexpr int v(int r) { return (r & 3) << 2; }
+};
+template <> struct Swz<64> {  // 128-byte rows: two rows per bank sweep
+  __device__ static constexpr int k(int r) { return (r >> 1) & 7; }
+  __device__ static constexpr int v(int r) { return ((r >> 1) & 1) << 2; }
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 ds_read_tr16(const unsigned char* p) {
+  v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+template <int D, int BC, int NW, bool MASKED>
+__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned char* kt_lds,
+                                              const unsigned char* vt_lds, const Frag<bf16_storage> (&qf)[D / 16],
+                                              f32x16_t (&o)[D / 32], float& m_run, float& l_run, int t0,
+                                              int qi, int n, int hf, int lane) {
+  constexpr int ROWB = D * 2;
+  // S^T = K Q^T
+  f32x16_t s[BC / 32];
+#pragma unroll
+  for (int kt = 0; kt < BC / 32; ++kt) {
+    s[kt] = f32x16_t{};
+    const int r = kt * 32 + n;
+    const unsigned char* krow = kt_lds + r * ROWB;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int c = (ks * 2 + hf) ^ Swz<D>::k(r);
+      mma(s[kt], Frag<bf16_storage>{*reinterpret_cast<const uint4*>(krow + c * 16)}, qf[ks]);
     }
   }
+  if constexpr (MASKED) {
+    // visible keys of this lane's query: local key index <= lim
+    const int lim = (a.diag ? min(qi, a.len - 1) : a.len - 1) - t0;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float4* dst = reinterpret_cast<float4*>(orow + dt * 32 + j * 8 + hf * 4);
-      float4 r = make_float4(o[dt][4 * j] * w_cur, o[dt][4 * j + 1] * w_cur, o[dt][4 * j + 2] * w_cur,
-                             o[dt][4 * j + 3] * w_cur);
-      if (!a.first) {
-        const float4 old = *dst;
-        r.x += w_old * old.x;
-        r.y += w_old * old.y;
-        r.z += w_old * old.z;
-        r.w += w_old * old.w;
+      for (int i = 0; i < 16; ++i)
+        if (kt * 32 + crow(i, hf) > lim) s[kt][i] = kNegInf;
+  }
+  // row max over this lane's 16*BC/32 keys, then across the two halves
+  float mx = kNegInf;
+#pragma unroll
+  for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
+  mx = fmaxf(mx, swap_halves(mx));
+  const float mxs = mx * a.scale_log2;
+  if (__builtin_amdgcn_ballot_w64(mxs > m_run + kRescaleThreshold) != 0) {
+    const float m_new = fmaxf(m_run, mxs);
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+  // P^T = exp2(S^T * scale - m) as bf16 fragments; the row sum is taken on the
+  // fp32 values so that lse (reused by the backward) is not perturbed by the
+  // bf16 rounding of P.
+  Frag<bf16_storage> pf[BC / 16];
+#pragma unroll
+  for (int kc = 0; kc < BC / 16; ++kc) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(__builtin_fmaf(s[kc >> 1][(kc & 1) * 8 + e], a.scale_log2, -m_use));
+      l_run += p[e];
+    }
+    pf[kc] = frag_from_f32<bf16_storage>(p);
+  }
+  // O^T += V^T P^T; A fragment = 2 transposed reads of 4 keys x 16 columns
+  const int g = lane >> 4, i16 = lane & 15;
+  const int hq = g >> 1;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int dcol = dt * 32 + (g & 1) * 16 + 4 * (i16 & 3);  // first of 4 columns this lane fetches
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      uint2 part[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = kc * 16 + u * 8 + hq * 4 + (i16 >> 2);
+        const int c = (dcol >> 3) ^ Swz<D>::v(r);
+        part[u] = ds_read_tr16(vt_lds + r * ROWB + c * 16 + (dcol & 7) * 2);
       }
-      *dst = r;
+      mma(o[dt], Frag<bf16_storage>{make_uint4(part[0].x, part[0].y, part[1].x, part[1].y)}, pf[kc]);
     }
-  if (hf == 0) *lsep = lse_new;
+  }
+}
+
+template <int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int STAGE = 2 * TILEB;
+  constexpr int RPI = 1024 / ROWB;  // rows per 1 KB load instruction
+  constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+  constexpr int IPW = BC / RPI / NW;  // load instructions per wave per tensor
+  static_assert(IPW >= 1 && (BC / RPI) % NW == 0, "tile rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int n = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int R = NW * 32 / a.hpw;
+  const int nrt = (a.len + R - 1) / R;
+  int rt = logical % nrt;
+  const int rest = logical / nrt;
+  const int hs = rest % a.hsub;
+  const int g = rest / a.hsub;
+  if (a.diag) rt = nrt - 1 - rt;
+  const int wpr = NW / a.hpw;
+  const int head = g * a.group + hs * a.hpw + wu / wpr;
+  const int row0 = rt * R + (wu % wpr) * 32;
+  const int qi = row0 + n;
+  const int wg_last_row = min(rt * R + R, a.len) - 1;
+  int ntiles = (a.len + BC - 1) / BC;
+  if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
+
+  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
+  const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
+  const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
+
+  Frag<bf16_storage> qf[D / 16];
+  {
+    const bf16_storage* qp =
+        reinterpret_cast<const bf16_storage*>(a.q) + (size_t)qi * qstride + (size_t)head * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[ks] = (qi < a.len) ? frag_load<bf16_storage>(qp + ks * 16) : frag_zero<bf16_storage>();
+  }
+  // Settle the Q loads here (vmcnt(0), other counters untouched), so that no
+  // wait for them is left inside the loop where it would also stall on the
+  // tile prefetch in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // every lane fetches one 16-byte chunk per instruction: row q*RPI + lane/CPR,
+  // LDS chunk slot lane%CPR, holding logical chunk slot ^ swizzle(row)
+  const int lrow = lane / CPR, slot = lane % CPR;
+  uint32_t koff[IPW], voff[IPW];  // byte offsets of this lane's chunks from the tile's first row
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wu * IPW + j) * RPI + lrow;
+    koff[j] = (uint32_t)(r * kvstride + (slot ^ Swz<D>::k(r)) * 8) * 2;
+    voff[j] = (uint32_t)(r * kvstride + (slot ^ Swz<D>::v(r)) * 8) * 2;
+  }
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
+  const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
+  auto issue = [&](int t0, unsigned char* kd) {  // kd: K tile, V tile follows
+    unsigned char* vd = kd + TILEB;
+    const size_t tb = (size_t)t0 * kvstride * 2;
+    if (t0 + BC <= a.len) {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int q = wu * IPW + j;
+        lds_dma16(kbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
+        lds_dma16(vbytes + tb + voff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
+      }
+    } else {  // ragged tail: rows past the end re-read the last row (masked later)
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int q = wu * IPW + j;
+        const int r = q * RPI + lrow;
+        const int row = min(t0 + r, a.len - 1);
+        const bf16_storage* ks = kbase + (size_t)row * kvstride + ((slot ^ Swz<D>::k(r)) * 8);
+        const bf16_storage* vs = vbase + (size_t)row * kvstride + ((slot ^ Swz<D>::v(r)) * 8);
+        lds_dma16(ks, __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
+        lds_dma16(vs, __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
+      }
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
+
+  // tiles [0, nfull) need no mask for any wave of this workgroup; the rest
+  // (diagonal band, ragged tail) take the masked instantiation
+  const int wg_first_row = rt * R;
+  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
+  issue(0, smem);
+  int t = 0;
+  for (; t < nfull; ++t) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile t has landed
+    __syncthreads();                                     // ... and everyone's; the other buffer is free
+    if (t + 1 < ntiles) issue((t + 1) * BC, smem + ((t + 1) & 1) * STAGE);
+    const unsigned char* rd = smem + (t & 1) * STAGE;
+    fwd_bf16_tile<D, BC, NW, false>(a, rd, rd + TILEB, qf, o, m_run, l_run, t * BC, qi, n, hf, lane);
+  }
+  for (; t < ntiles; ++t) {
+    const int t0 = t * BC;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t0 + BC, smem + ((t + 1) & 1) * STAGE);
+    if (a.diag && t0 > row0 + 31) continue;  // wholly above this wave's rows (uniform)
+    const unsigned char* rd = smem + (t & 1) * STAGE;
+    fwd_bf16_tile<D, BC, NW, true>(a, rd, rd + TILEB, qf, o, m_run, l_run, t0, qi, n, hf, lane);
+  }
+  fwd_epilogue<D>(a, o, m_run, l_run, head, qi, hf);
 }
 
 template <typename T, int D, int BC, int NW>
@@ -292,15 +502,27 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = RA_FWD_WAVES;
+// Both paths must share the wave count: the host derives the head packing from it.
+constexpr int kF32Waves = kFwdWaves;
+
+template <int D, int BC, int NW>
+static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
+  if (a.hpw < 1 || a.hsub < 1 || NW % a.hpw != 0) return hipErrorInvalidValue;
+  const int R = NW * 32 / a.hpw;
+  const int nblk = ((a.len + R - 1) / R) * a.hsub * a.hkv;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW>), dim3(nblk), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
   if (elem_bytes == 2) {
-    if (head_dim == 64) return launch_fwd_t<bf16_storage, 64, 64, kFwdWaves>(a, st);
-    if (head_dim == 128) return launch_fwd_t<bf16_storage, 128, 64, kFwdWaves>(a, st);
+    if (head_dim == 64) return launch_fwd_bf16<64, RA_FWD_BC, kFwdWaves>(a, st);
+    if (head_dim == 128) return launch_fwd_bf16<128, RA_FWD_BC, kFwdWaves>(a, st);
   } else {
-    if (head_dim == 64) return launch_fwd_t<float, 64, 64, kFwdWaves>(a, st);
-    if (head_dim == 128) return launch_fwd_t<float, 128, 32, kFwdWaves>(a, st);
+    if (head_dim == 64) return launch_fwd_t<float, 64, 64, kF32Waves>(a, st);
+    if (head_dim == 128) return launch_fwd_t<float, 128, 32, kF32Waves>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -115,6 +115,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// Global -> LDS copy of 16 bytes per lane by the load unit (LDS DMA): lane i's
+// 16 bytes land at LDS byte address lds_base + 16*i.  Written as inline asm on
+// purpose: with the compiler's intrinsic, the wait-count pass cannot tell which
+// LDS bytes the copy writes and stalls every later LDS read until the copy
+// completes, which serialises the prefetch of the next tile against the reads
+// of the current one.  The asm has no register outputs; callers make the data
+// visible with `s_waitcnt vmcnt(0)` followed by a workgroup barrier.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // XCD-aware work order: the dispatcher deals workgroups round-robin over the
 // 8 XCDs, so consecutive logical tiles (which share K/V) are remapped onto
 // one XCD and its L2.
