@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--workload", default="causal_128k_h32_d128")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=48, help="query rows in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU oracle sample")
     return p.parse_args()
 
 

@@ -1,0 +1,396 @@
+// bf16 backward ring-step kernels for gfx950 (the fp32 twins live in bwd_step.hip).
+//
+// Gradients of exact attention over one K/V block, recomputing the
+// probabilities from the forward's log-sum-exp: with S = Q K^T / sqrt(d),
+// P = exp(S - lse), dP = dO V^T, dS = P * (dP - Delta):
+//   dQ += dS K / sqrt(d),   dK += dS^T Q / sqrt(d),   dV += P^T dO.
+// (The ring runs in every layer of training -- close-reading notes on "Ring
+// Attention with Blockwise Transformers for Near-Infinite Context", §3.5 --
+// so the same rotated K/V blocks drive the backward.)
+//
+// Same building blocks as the bf16 forward: streamed tiles are copied
+// global -> LDS by LDS DMA into unpadded, XOR-swizzled rows; operands whose
+// contraction index runs along the tile rows are read with transposed LDS
+// reads (tr_frag) instead of being stored twice; diagonal-band and ragged
+// tiles run in separate (masked) loops so the hot loop carries no masking.
+//
+//  * dK/dV kernel: a wave owns 32 keys (K, V in registers as B operands, keys
+//    on lanes) and walks the query tiles of every query head of its group.
+//    S and dP come out with keys on lanes, so P and dS are B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposed reads
+//    of the streamed Q and dO tiles.  The row terms (lse, Delta) of a tile
+//    ride along in LDS.
+//  * dQ kernel: a wave owns 32 query rows (Q, dO in registers, queries on
+//    lanes, lse and Delta per-lane scalars) and walks the K/V tiles; dQ^T +=
+//    K^T dS^T reads K transposed from the same K tile used for S^T.
+#include <type_traits>
+
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace ra {
+
+namespace {
+
+#ifndef RA_BWD_NW
+#define RA_BWD_NW 8
+#endif
+#ifndef RA_KV_NW
+#define RA_KV_NW 4
+#endif
+constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
+constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: one wave per SIMD (accumulators need >256 registers)
+
+// LDS DMA of rows [t0, t0 + ROWS) of a token-major [len][heads][D] bf16 tensor
+// (head offset already applied) into a swizzled [ROWS][D] tile.  Each wave
+// moves ROWS/NW * D*2 bytes, 1 KB per instruction; rows past `len` re-read
+// row len-1 (their contribution is masked by the caller).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(const bf16_storage* base, size_t stride, int t0, int len,
+                                         unsigned char* tile, int wu, int lane) {
+  constexpr int ROWB = D * 2, RPI = 1024 / ROWB, CPR = ROWB / 16;
+  constexpr int NI = ROWS / RPI;  // 1 KB instructions per tile
+  static_assert(NI % NW == 0 || NI < NW, "tile instructions must spread over the waves");
+  constexpr int IPW = (NI + NW - 1) / NW;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int q = wu * IPW + j;
+    if (NI % NW != 0 && q >= NI) break;  // uniform
+    const int r = q * RPI + lane / CPR, slot = lane % CPR;
+    const int row = min(t0 + r, len - 1);
+    const bf16_storage* src = base + (size_t)row * stride + ((slot ^ swz<D>(r)) * 8);
+    lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tile + q * 1024)));
+  }
+}
+
+}  // namespace
+
+// =================================================================== dK / dV
+template <int D, int BR, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BR * ROWB;
+  constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
+  static_assert(BR % 32 == 0 && (BR == 32 || BR % 64 == 0), "row-term DMA covers 64 dwords per wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int KW = NW * 32;
+  const int nkt = (a.len + KW - 1) / KW;
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int kt = logical % nkt;  // ascending: with a causal diagonal, low key tiles are heaviest
+  const int g = logical / nkt;
+  const int kb0 = kt * KW;
+  const int key0 = kb0 + wu * 32;
+  const int key = key0 + n;
+  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
+
+  Frag<bf16_storage> kf[D / 16], vf[D / 16];
+  {
+    const int kr = min(key, a.len - 1);  // lanes past the end compute garbage that is never stored
+    const bf16_storage* kp = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
+    const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = frag_load<bf16_storage>(kp + ks * 16);
+      vf[ks] = frag_load<bf16_storage>(vp + ks * 16);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // settle the K/V loads before the pipelined loop
+
+  f32x16_t dkT[D / 32], dvT[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dkT[dt] = f32x16_t{};
+    dvT[dt] = f32x16_t{};
+  }
+
+  const int nqt = (a.len + BR - 1) / BR;
+  const int qt_lo = a.diag ? kb0 / BR : 0;                        // earlier tiles: every key is in their future
+  const int qt_nb = a.diag ? min(nqt, (kb0 + KW - 1 + BR - 1) / BR) : qt_lo;  // end of the diagonal band
+  const int qt_full = max(qt_nb, a.len / BR);                     // ragged tail from here
+  const int per_head = nqt - qt_lo;
+  const int iters = per_head * a.group;
+
+  auto issue = [&](int it, unsigned char* st) {
+    const int hh = it / per_head, qt = qt_lo + it % per_head;
+    const int head = g * a.group + hh;
+    const int r0 = qt * BR;
+    dma_tile<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.q) + (size_t)head * D, qstride, r0, a.len, st, wu, lane);
+    dma_tile<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.dout) + (size_t)head * D, qstride, r0, a.len,
+                        st + TILEB, wu, lane);
+    // row terms [lse2(BR) | Delta(BR)]: the last waves move 64 dwords each
+    constexpr int NRW = (2 * BR + 63) / 64;
+    static_assert(NRW <= NW, "row terms need more waves than the workgroup has");
+    const int k = wu - (NW - NRW);
+    if (k >= 0) {  // uniform
+      const int e = k * 64 + lane;
+      const int r = min(r0 + (e % BR), a.len - 1);
+      const float* src = (e < BR ? a.lse2 : a.delta) + (size_t)head * a.len + r;
+      lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_addr(st + 2 * TILEB + k * 256)));
+    }
+  };
+
+  auto tile = [&](int it, const unsigned char* st, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int qt = qt_lo + it % per_head;
+    const int r0 = qt * BR;
+    const unsigned char* qn = st;
+    const unsigned char* dn = st + TILEB;
+    const float* rt = reinterpret_cast<const float*>(st + 2 * TILEB);
+    if (MASKED && a.diag && key0 > r0 + BR - 1) return;  // every row precedes this wave's keys
+#pragma unroll
+    for (int qs = 0; qs < BR / 32; ++qs) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), kf[ks]);
+        mma(dp, row_frag<D>(dn, qs * 32 + n, ks, hf), vf[ks]);
+      }
+      float p[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 l4 = *reinterpret_cast<const float4*>(rt + qs * 32 + j * 8 + hf * 4);
+        const float4 d4 = *reinterpret_cast<const float4*>(rt + BR + qs * 32 + j * 8 + hf * 4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          float pv = fast_exp2(__builtin_fmaf(s[i], a.scale_log2, -lv[e]));
+          if constexpr (MASKED) {
+            const int row = r0 + qs * 32 + crow(i, hf);
+            if (row >= a.len || (a.diag && key > row)) pv = 0.f;
+          }
+          p[i] = pv;
+          dp[i] = pv * (dp[i] - dv[e]);  // dS
+        }
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        float ds8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ds8[e] = dp[c2 * 8 + e];
+        const Frag<bf16_storage> pf = frag_from_f32<bf16_storage>(p + c2 * 8);
+        const Frag<bf16_storage> sf = frag_from_f32<bf16_storage>(ds8);
+        const int kc = qs * 2 + c2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          mma(dvT[dt], tr_frag<D>(dn, dt * 32, kc, lane), pf);
+          mma(dkT[dt], tr_frag<D>(qn, dt * 32, kc, lane), sf);
+        }
+      }
+    }
+  };
+
+  auto step = [&](int it, auto masked_tag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` has landed
+    __syncthreads();                                     // ... everyone's; the other stage is free
+    if (it + 1 < iters) issue(it + 1, smem + ((it + 1) & 1) * STAGE);
+    tile(it, smem + (it & 1) * STAGE, masked_tag);
+  };
+
+  if (iters > 0) issue(0, smem);
+  int it = 0;
+  for (int hh = 0; hh < a.group; ++hh) {
+    const int base = hh * per_head - qt_lo;  // it = base + qt
+    for (; it < base + qt_nb; ++it) step(it, std::true_type{});
+    for (; it < base + qt_full; ++it) step(it, std::false_type{});
+    for (; it < base + nqt; ++it) step(it, std::true_type{});
+  }
+
+  if (key >= a.len) return;
+  float* dkp = a.dk + (size_t)key * kvstride + (size_t)g * D;
+  float* dvp = a.dv + (size_t)key * kvstride + (size_t)g * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = dt * 32 + j * 8 + hf * 4;
+      float4* pk = reinterpret_cast<float4*>(dkp + d0);
+      float4* pv = reinterpret_cast<float4*>(dvp + d0);
+      float4 ok = *pk, ov = *pv;
+      ok.x += a.scale * dkT[dt][4 * j];
+      ok.y += a.scale * dkT[dt][4 * j + 1];
+      ok.z += a.scale * dkT[dt][4 * j + 2];
+      ok.w += a.scale * dkT[dt][4 * j + 3];
+      ov.x += dvT[dt][4 * j];
+      ov.y += dvT[dt][4 * j + 1];
+      ov.z += dvT[dt][4 * j + 2];
+      ov.w += dvT[dt][4 * j + 3];
+      *pk = ok;
+      *pv = ov;
+    }
+}
+
+// =================================================================== dQ
+template <int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int STAGE = 2 * TILEB;  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int R = NW * 32 / a.hpw;
+  const int nrt = (a.len + R - 1) / R;
+  int rt = logical % nrt;
+  const int rest = logical / nrt;
+  const int hs = rest % a.hsub;
+  const int g = rest / a.hsub;
+  if (a.diag) rt = nrt - 1 - rt;  // longest row tiles first
+  const int wpr = NW / a.hpw;
+  const int head = g * a.group + hs * a.hpw + wu / wpr;
+  const int row0 = rt * R + (wu % wpr) * 32;
+  const int qi = row0 + n;
+  const int wg_first_row = rt * R;
+  const int wg_last_row = min(rt * R + R, a.len) - 1;
+  int ntiles = (a.len + BC - 1) / BC;
+  if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
+  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
+
+  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
+  Frag<bf16_storage> qf[D / 16], of[D / 16];
+  {
+    const int qr = min(qi, a.len - 1);
+    const bf16_storage* qp = reinterpret_cast<const bf16_storage*>(a.q) + (size_t)qr * qstride + (size_t)head * D + hf * 8;
+    const bf16_storage* op = reinterpret_cast<const bf16_storage*>(a.dout) + (size_t)qr * qstride + (size_t)head * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = frag_load<bf16_storage>(qp + ks * 16);
+      of[ks] = frag_load<bf16_storage>(op + ks * 16);
+    }
+  }
+  const float lse2 = a.lse2[(size_t)head * a.len + min(qi, a.len - 1)];
+  const float dlt = a.delta[(size_t)head * a.len + min(qi, a.len - 1)];
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  f32x16_t dqT[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dqT[dt] = f32x16_t{};
+
+  const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
+  const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
+  auto issue = [&](int t, unsigned char* st) {
+    dma_tile<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
+    dma_tile<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
+  };
+
+  auto tile = [&](int t, const unsigned char* st, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int t0 = t * BC;
+    const unsigned char* kn = st;
+    const unsigned char* vn = st + TILEB;
+    if (MASKED && a.diag && t0 > row0 + 31) return;  // wholly in this wave's future
+    f32x16_t s[BC / 32], dp[BC / 32];
+#pragma unroll
+    for (int kt = 0; kt < BC / 32; ++kt) {
+      s[kt] = f32x16_t{};
+      dp[kt] = f32x16_t{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        mma(s[kt], row_frag<D>(kn, kt * 32 + n, ks, hf), qf[ks]);
+        mma(dp[kt], row_frag<D>(vn, kt * 32 + n, ks, hf), of[ks]);
+      }
+    }
+    const int lim = (a.diag ? min(qi, a.len - 1) : a.len - 1) - t0;  // visible local keys: <= lim
+#pragma unroll
+    for (int kt = 0; kt < BC / 32; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float pv = fast_exp2(__builtin_fmaf(s[kt][i], a.scale_log2, -lse2));
+        if constexpr (MASKED) {
+          if (kt * 32 + crow(i, hf) > lim) pv = 0.f;
+        }
+        dp[kt][i] = pv * (dp[kt][i] - dlt);  // dS^T
+      }
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      float ds8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ds8[e] = dp[kc >> 1][(kc & 1) * 8 + e];
+      const Frag<bf16_storage> sf = frag_from_f32<bf16_storage>(ds8);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) mma(dqT[dt], tr_frag<D>(kn, dt * 32, kc, lane), sf);
+    }
+  };
+
+  auto step = [&](int t, auto masked_tag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * STAGE);
+    tile(t, smem + (t & 1) * STAGE, masked_tag);
+  };
+
+  issue(0, smem);
+  int t = 0;
+  for (; t < nfull; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
+
+  if (qi >= a.len) return;
+  float* dqp = a.dq + (size_t)qi * qstride + (size_t)head * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4* p = reinterpret_cast<float4*>(dqp + dt * 32 + j * 8 + hf * 4);
+      float4 r = make_float4(a.scale * dqT[dt][4 * j], a.scale * dqT[dt][4 * j + 1], a.scale * dqT[dt][4 * j + 2],
+                             a.scale * dqT[dt][4 * j + 3]);
+      if (!a.first) {
+        const float4 o = *p;
+        r.x += o.x;
+        r.y += o.y;
+        r.z += o.z;
+        r.w += o.w;
+      }
+      *p = r;
+    }
+}
+
+#ifndef RA_BWD_BR
+#define RA_BWD_BR 32
+#endif
+#ifndef RA_BWD_BC
+#define RA_BWD_BC 32
+#endif
+
+template <int D>
+static hipError_t launch_dkdv_bf16_t(const BwdArgs& a, hipStream_t st) {
+  const int KW = kKvNW * 32;
+  const int nblk = ((a.len + KW - 1) / KW) * a.hkv;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW>), dim3(nblk), dim3(kKvNW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dq_bf16_t(const BwdArgs& a, hipStream_t st) {
+  if (a.hpw < 1 || a.hsub < 1 || kBwdNW % a.hpw != 0) return hipErrorInvalidValue;
+  const int R = kBwdNW * 32 / a.hpw;
+  const int nblk = ((a.len + R - 1) / R) * a.hsub * a.hkv;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, RA_BWD_BC, kBwdNW>), dim3(nblk), dim3(kBwdNW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t st) {
+  if (head_dim == 64) return launch_dkdv_bf16_t<64>(a, st);
+  if (head_dim == 128) return launch_dkdv_bf16_t<128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int head_dim, hipStream_t st) {
+  if (head_dim == 64) return launch_dq_bf16_t<64>(a, st);
+  if (head_dim == 128) return launch_dq_bf16_t<128>(a, st);
+  return hipErrorInvalidValue;
+}
+
+int bwd_bf16_waves_per_block() { return kBwdNW; }
+
+}  // namespace ra

@@ -360,6 +360,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
+  if (elem_bytes == 2) return launch_bwd_dkdv_bf16(a, head_dim, st);
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dkdv_t<bf16_storage, 64, 32>(a, st);
     if (head_dim == 128) return launch_dkdv_t<bf16_storage, 128, RA_KV_BR>(a, st);
@@ -371,6 +372,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipSt
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
+  if (elem_bytes == 2) return launch_bwd_dq_bf16(a, head_dim, st);
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dq_t<bf16_storage, 64, 32>(a, st);
     if (head_dim == 128) return launch_dq_t<bf16_storage, 128, RA_DQ_BC>(a, st);

@@ -276,23 +276,6 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
 //    on almost every tile.  Results are exact either way: the reference max
 //    cancels in the final normalisation.
 // ============================================================================
-template <int D> struct Swz;
-template <> struct Swz<128> {  // 256-byte rows: one row spans all 64 banks
-  __device__ static constexpr int k(int r) { return r & 15; }
-  __device__ static constexpr int v(int r) { return (r & 3) << 2; }
-};
-template <> struct Swz<64> {  // 128-byte rows: two rows per bank sweep
-  __device__ static constexpr int k(int r) { return (r >> 1) & 7; }
-  __device__ static constexpr int v(int r) { return ((r >> 1) & 1) << 2; }
-};
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint2 ds_read_tr16(const unsigned char* p) {
-  v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D, int BC, int NW, bool MASKED>
@@ -306,13 +289,8 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
 #pragma unroll
   for (int kt = 0; kt < BC / 32; ++kt) {
     s[kt] = f32x16_t{};
-    const int r = kt * 32 + n;
-    const unsigned char* krow = kt_lds + r * ROWB;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int c = (ks * 2 + hf) ^ Swz<D>::k(r);
-      mma(s[kt], Frag<bf16_storage>{*reinterpret_cast<const uint4*>(krow + c * 16)}, qf[ks]);
-    }
+    for (int ks = 0; ks < D / 16; ++ks) mma(s[kt], row_frag<D>(kt_lds, kt * 32 + n, ks, hf), qf[ks]);
   }
   if constexpr (MASKED) {
     // visible keys of this lane's query: local key index <= lim
@@ -357,23 +335,10 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
     pf[kc] = frag_from_f32<bf16_storage>(p);
   }
   // O^T += V^T P^T; A fragment = 2 transposed reads of 4 keys x 16 columns
-  const int g = lane >> 4, i16 = lane & 15;
-  const int hq = g >> 1;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int dcol = dt * 32 + (g & 1) * 16 + 4 * (i16 & 3);  // first of 4 columns this lane fetches
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int kc = 0; kc < BC / 16; ++kc) {
-      uint2 part[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r = kc * 16 + u * 8 + hq * 4 + (i16 >> 2);
-        const int c = (dcol >> 3) ^ Swz<D>::v(r);
-        part[u] = ds_read_tr16(vt_lds + r * ROWB + c * 16 + (dcol & 7) * 2);
-      }
-      mma(o[dt], Frag<bf16_storage>{make_uint4(part[0].x, part[0].y, part[1].x, part[1].y)}, pf[kc]);
-    }
-  }
+    for (int kc = 0; kc < BC / 16; ++kc) mma(o[dt], tr_frag<D>(vt_lds, dt * 32, kc, lane), pf[kc]);
 }
 
 template <int D, int BC, int NW>
@@ -428,12 +393,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   // every lane fetches one 16-byte chunk per instruction: row q*RPI + lane/CPR,
   // LDS chunk slot lane%CPR, holding logical chunk slot ^ swizzle(row)
   const int lrow = lane / CPR, slot = lane % CPR;
-  uint32_t koff[IPW], voff[IPW];  // byte offsets of this lane's chunks from the tile's first row
+  uint32_t koff[IPW];  // byte offsets of this lane's chunks from the tile's first row
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int r = (wu * IPW + j) * RPI + lrow;
-    koff[j] = (uint32_t)(r * kvstride + (slot ^ Swz<D>::k(r)) * 8) * 2;
-    voff[j] = (uint32_t)(r * kvstride + (slot ^ Swz<D>::v(r)) * 8) * 2;
+    koff[j] = (uint32_t)(r * kvstride + (slot ^ swz<D>(r)) * 8) * 2;
   }
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
@@ -445,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
       for (int j = 0; j < IPW; ++j) {
         const int q = wu * IPW + j;
         lds_dma16(kbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
-        lds_dma16(vbytes + tb + voff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
+        lds_dma16(vbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
       }
     } else {  // ragged tail: rows past the end re-read the last row (masked later)
 #pragma unroll
@@ -453,8 +417,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
         const int q = wu * IPW + j;
         const int r = q * RPI + lrow;
         const int row = min(t0 + r, a.len - 1);
-        const bf16_storage* ks = kbase + (size_t)row * kvstride + ((slot ^ Swz<D>::k(r)) * 8);
-        const bf16_storage* vs = vbase + (size_t)row * kvstride + ((slot ^ Swz<D>::v(r)) * 8);
+        const bf16_storage* ks = kbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
+        const bf16_storage* vs = vbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
         lds_dma16(ks, __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
         lds_dma16(vs, __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
       }

@@ -129,8 +129,72 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) 
                : "memory", "m0");
 }
 
+// Same, 4 bytes per lane (lane i's dword lands at lds_base + 4*i).
+__device__ __forceinline__ void lds_dma4(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// XOR swizzle of the 16-byte chunks of an unpadded [rows][D] bf16 tile in LDS
+// (row r stores logical chunk c at chunk slot c ^ swz(r)).  Chosen so that both
+// ways the kernels read such a tile are bank-conflict free on the 64 x 4-byte
+// LDS banks:
+//  * ds_read_b128 of one chunk by 16 consecutive rows (MFMA operand with k = D)
+//    -- swz is a bijection on every 16 consecutive rows (D=128) or on every 8
+//    row pairs (D=64, two 128-byte rows per bank sweep);
+//  * ds_read_b64_tr_b16 of 4 (x2) consecutive rows by 4 consecutive chunks
+//    (transposed operand) -- the high bits of swz spread such row quads over
+//    different 64-byte bank groups.
+template <int D> __device__ __forceinline__ constexpr int swz(int r);
+template <> __device__ __forceinline__ constexpr int swz<128>(int r) {
+  return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+template <> __device__ __forceinline__ constexpr int swz<64>(int r) {
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane j
+// receives element k (k = 0..3) = the 16-bit value at byte (address of lane
+// 4k + j/4) + 2*(j%4).  With lane i pointing at row base+i/4, column
+// c0 + 4*(i%4) of a row-major bf16 tile, lane j thus gets rows base..base+3 of
+// column c0 + j: four consecutive k values of one operand row.
+__device__ __forceinline__ uint2 ds_read_tr16(const unsigned char* p) {
+  v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// A operand (rows = tile column, k = 16 tile rows) of a 32x32x16 MFMA read
+// transposed from a swizzled [rows][D] bf16 tile: lane l covers operand row
+// (column of the tile) col0 + l%32 and tile rows kc*16 + {h*4..h*4+3,
+// 8+h*4..8+h*4+3} (h = l/32), the order in which a 32x32 accumulator hands
+// its rows to a B operand (see perm16).
+template <int D>
+__device__ __forceinline__ Frag<bf16_storage> tr_frag(const unsigned char* tile, int col0, int kc, int lane) {
+  const int g = lane >> 4, i16 = lane & 15;
+  const int dcol = col0 + (g & 1) * 16 + 4 * (i16 & 3);
+  uint2 part[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = kc * 16 + u * 8 + (g >> 1) * 4 + (i16 >> 2);
+    const int c = (dcol >> 3) ^ swz<D>(r);
+    part[u] = ds_read_tr16(tile + r * (D * 2) + c * 16 + (dcol & 7) * 2);
+  }
+  return Frag<bf16_storage>{make_uint4(part[0].x, part[0].y, part[1].x, part[1].y)};
+}
+
+// B or A operand with k = D from a swizzled [rows][D] bf16 tile: row r, k slice ks.
+template <int D>
+__device__ __forceinline__ Frag<bf16_storage> row_frag(const unsigned char* tile, int r, int ks, int hf) {
+  const int c = (ks * 2 + hf) ^ swz<D>(r);
+  return Frag<bf16_storage>{*reinterpret_cast<const uint4*>(tile + r * (D * 2) + c * 16)};
 }
 
 // XCD-aware work order: the dispatcher deals workgroups round-robin over the

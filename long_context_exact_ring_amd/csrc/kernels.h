@@ -29,7 +29,9 @@ int fwd_waves_per_block();
 struct BwdPreArgs {
   const void* dout;  // [len][hq][D] bf16 or fp32
   const float* out;  // [len][hq][D]
-  float* delta;      // [hq][len]
+  const float* lse;  // [hq][len]
+  float* delta;      // [hq][len]  Delta = rowsum(dout * out)
+  float* lse2;       // [hq][len]  lse * log2(e)
   int len, hq;
 };
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hipStream_t st);
@@ -42,6 +44,7 @@ struct BwdArgs {
   const void* dout;  // [len][hq][D]
   const float* lse;  // [hq][len]
   const float* delta;  // [hq][len]
+  const float* lse2;   // [hq][len] lse * log2(e)
   float* dq;         // [len][hq][D]   (overwrite when first != 0, else accumulate)
   float* dk;         // [len][hkv][D]  (accumulate)
   float* dv;         // [len][hkv][D]  (accumulate)
@@ -55,6 +58,10 @@ struct BwdArgs {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 int bwd_dq_waves_per_block();
+// bf16 fast paths (LDS-DMA staging, transposed operand reads)
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int head_dim, hipStream_t st);
+int bwd_bf16_waves_per_block();
 
 // Pairwise merge of two normalised partials.
 struct MergeArgs {

@@ -7,7 +7,8 @@
 // o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.  HBM-bound, VALU only.
 //
 // Backward preprocess: Delta_i = sum_d dout_i * out_i for every (head, row),
-// the row term of dS = P * (dP - Delta).  One wavefront per (row, head).
+// the row term of dS = P * (dP - Delta), and lse in log2 units (the exponent
+// offset the backward kernels use).  One wavefront per (row, head).
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -80,7 +81,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) a.delta[(long)h * a.len + r] = acc;
+  if (lane == 0) {
+    a.delta[(long)h * a.len + r] = acc;
+    a.lse2[(long)h * a.len + r] = a.lse[(long)h * a.len + r] * kLog2e;
+  }
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hipStream_t st) {

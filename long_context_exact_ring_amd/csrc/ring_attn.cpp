@@ -395,15 +395,17 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   Ctx* c = nullptr;
   if ((st = get_ctx(&c)) != RA_OK) return st;
   ++g_prof_call;
-  if ((st = ensure_delta(c, sh.lse_bytes())) != RA_OK) return st;
+  if ((st = ensure_delta(c, 2 * sh.lse_bytes())) != RA_OK) return st;
+  float* lse2 = c->delta + (size_t)sh.block_len * sh.heads;
   {
-    BwdPreArgs p{dout, out, c->delta, sh.block_len, sh.heads};
+    BwdPreArgs p{dout, out, lse, c->delta, lse2, sh.block_len, sh.heads};
     ProfScope ps(KIND_PRE, stream);
     RA_HIP(launch_bwd_pre(p, sh.elem_bytes, sh.head_dim, stream));
   }
   const float scale = rsqrt_dim(sh.head_dim);
   const int group = sh.heads / sh.kv_heads;
-  const int hpw = heads_per_block(group, bwd_dq_waves_per_block());
+  const int hpw =
+      heads_per_block(group, sh.elem_bytes == 2 ? bwd_bf16_waves_per_block() : bwd_dq_waves_per_block());
   auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
     BwdArgs a{};
     a.q = q;
@@ -412,6 +414,7 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
     a.dout = dout;
     a.lse = lse;
     a.delta = c->delta;
+    a.lse2 = lse2;
     a.dq = dq;
     a.dk = dkb[j];
     a.dv = dvb[j];
