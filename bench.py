@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU oracle sample")
+    p.add_argument("--copy-ref-mib", type=int, default=0,
+                   help="before timing, run one plain device copy of this many MiB (a reference kernel of "
+                        "known traffic for scaling profiler byte counters)")
     return p.parse_args()
 
 
@@ -105,6 +108,30 @@ def cpu_baseline(w, rows: int):
             "seconds": dt}
 
 
+def profiled_traffic(kind: str, head_dim: int, dtype: str):
+    """HBM bytes per dispatch of a kernel from the committed profiler summary, or None.
+
+    profiles/traffic.json holds FETCH_SIZE/WRITE_SIZE-derived bytes (scaled by a
+    reference copy) together with hashes of the kernel sources they were taken
+    with; any source change since then makes the figure stale (None).
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if dtype != "bf16" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    for fname, sha in rec.get("source_sha256", {}).items():
+        src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+            return None
+    pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel"}.get(kind)
+    for name, t in rec.get("kernels", {}).items():
+        if pattern and pattern in name and f"<{head_dim}," in name:
+            return round(t["read_bytes"] + t["write_bytes"])
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +165,15 @@ def main():
                 ra.bwd(qs[r], kb, vb, outs[r], dos[r], lses[r], causal=w.causal, rank=r, dq=dqs[r],
                        dk_blocks=dkb, dv_blocks=dvb)
 
+    if args.copy_ref_mib > 0:
+        nbytes = args.copy_ref_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy: {nbytes} bytes read + {nbytes} bytes written")
+        del src, dst
     for i in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -178,7 +214,8 @@ def main():
     dom_ms = kern.get(dom, {}).get("ms_per_step", float("nan"))
     achieved = alg[dom] / (dom_ms * 1e-3) / 1e12 if dom in kern else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": (achieved / peak) if achieved else None, "traffic": None}
+                "frac": (achieved / peak) if achieved else None,
+                "traffic": profiled_traffic(dom, d, w.dtype)}
 
     overlap = {"copy_ms_per_step": copy_ms / args.steps, "hidden_ms_per_step": hidden_ms / args.steps,
                "hidden_frac": (hidden_ms / copy_ms) if copy_ms > 0 else None,

@@ -65,6 +65,20 @@ def _softmax_rows(s: np.ndarray):
     return p, lse
 
 
+def _visible_prefix(causal: bool, q_pos_chunk: np.ndarray, k_pos: np.ndarray) -> int:
+    """Number of leading keys that can be visible to a row chunk.
+
+    With a causal mask a row only sums over keys at positions <= its own
+    (the definition's visible set), so keys past the chunk's last position
+    contribute exact zeros and are left out.  Requires sorted key positions;
+    otherwise every key is kept.
+    """
+    m = k_pos.shape[0]
+    if not causal or m == 0 or np.any(np.diff(k_pos) < 0):
+        return m
+    return int(np.searchsorted(k_pos, q_pos_chunk.max(), side="right"))
+
+
 def _defaults(n: int, m: int, q_pos, k_pos):
     if q_pos is None:
         q_pos = np.arange(n, dtype=np.int64)
@@ -95,10 +109,13 @@ def attention_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,
         vg = np.asarray(v[:, g, :], dtype=np.float64)
         for r0 in range(0, n, chunk):
             r1 = min(n, r0 + chunk)
+            kv = _visible_prefix(causal, q_pos[r0:r1], k_pos)
+            if kv == 0:
+                continue  # no visible key: out stays 0, lse stays -inf
             qh = np.asarray(q[r0:r1, h, :], dtype=np.float64)
-            s = _scores(qh, kg, scale, causal, q_pos[r0:r1], k_pos)
+            s = _scores(qh, kg[:kv], scale, causal, q_pos[r0:r1], k_pos[:kv])
             p, lse[h, r0:r1] = _softmax_rows(s)
-            out[r0:r1, h, :] = p @ vg
+            out[r0:r1, h, :] = p @ vg[:kv]
     return out, lse
 
 
@@ -132,18 +149,21 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
         vg = np.asarray(v[:, g, :], dtype=np.float64)
         for r0 in range(0, n, chunk):
             r1 = min(n, r0 + chunk)
+            kv = _visible_prefix(causal, q_pos[r0:r1], k_pos)
+            if kv == 0:
+                continue  # no visible key: no output, no gradient
             qh = np.asarray(q[r0:r1, h, :], dtype=np.float64)
             doh = np.asarray(dout[r0:r1, h, :], dtype=np.float64)
-            s = _scores(qh, kg, scale, causal, q_pos[r0:r1], k_pos)
+            s = _scores(qh, kg[:kv], scale, causal, q_pos[r0:r1], k_pos[:kv])
             p, lse[h, r0:r1] = _softmax_rows(s)
-            oh = p @ vg
+            oh = p @ vg[:kv]
             out[r0:r1, h, :] = oh
-            dv[:, g, :] += p.T @ doh
-            dp = doh @ vg.T
+            dv[:kv, g, :] += p.T @ doh
+            dp = doh @ vg[:kv].T
             delta = np.sum(doh * oh, axis=1)
             ds = p * (dp - delta[:, None])
-            dq[r0:r1, h, :] = (ds @ kg) * scale
-            dk[:, g, :] += (ds.T @ qh) * scale
+            dq[r0:r1, h, :] = (ds @ kg[:kv]) * scale
+            dk[:kv, g, :] += (ds.T @ qh) * scale
     return dq, dk, dv, out, lse
 
 
