@@ -36,10 +36,13 @@ namespace {
 #define RA_BWD_NW 8
 #endif
 #ifndef RA_KV_NW
-#define RA_KV_NW 4
+#define RA_KV_NW 8
+#endif
+#ifndef RA_KV_KLDS
+#define RA_KV_KLDS 1
 #endif
 constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
-constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: one wave per SIMD (accumulators need >256 registers)
+constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per SIMD; K rows read from LDS)
 
 // LDS DMA of rows [t0, t0 + ROWS) of a token-major [len][heads][D] bf16 tensor
 // (head offset already applied) into a swizzled [ROWS][D] tile.  Each wave
@@ -66,13 +69,15 @@ __device__ __forceinline__ void dma_tile(const bf16_storage* base, size_t stride
 }  // namespace
 
 // =================================================================== dK / dV
-template <int D, int BR, int NW>
+template <int D, int BR, int NW, bool KLDS>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BR * ROWB;
   constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
+  constexpr int KTB = KLDS ? NW * 32 * ROWB : 16;  // the workgroup's K rows (KLDS: read from LDS)
   static_assert(BR % 32 == 0 && (BR == 32 || BR % 64 == 0), "row-term DMA covers 64 dwords per wave");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ktile[KTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 31, hf = lane >> 5;
@@ -88,16 +93,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int key = key0 + n;
   const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
 
-  Frag<bf16_storage> kf[D / 16], vf[D / 16];
+  Frag<bf16_storage> kf[KLDS ? 1 : D / 16], vf[D / 16];
   {
     const int kr = min(key, a.len - 1);  // lanes past the end compute garbage that is never stored
     const bf16_storage* kp = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
     const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = frag_load<bf16_storage>(kp + ks * 16);
+      if constexpr (!KLDS) kf[ks] = frag_load<bf16_storage>(kp + ks * 16);
       vf[ks] = frag_load<bf16_storage>(vp + ks * 16);
     }
+  }
+  if constexpr (KLDS) {  // the workgroup's K rows go to LDS once; waves read their 32 rows as B operands
+    dma_tile<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
+                             ktile, wu, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // settle the K/V loads before the pipelined loop
 
@@ -147,7 +158,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), kf[ks]);
+        if constexpr (KLDS)
+          mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), row_frag<D>(ktile, wu * 32 + n, ks, hf));
+        else
+          mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), kf[ks]);
         mma(dp, row_frag<D>(dn, qs * 32 + n, ks, hf), vf[ks]);
       }
       float p[16];
@@ -365,7 +379,8 @@ static hipError_t launch_dkdv_bf16_t(const BwdArgs& a, hipStream_t st) {
   const int KW = kKvNW * 32;
   const int nblk = ((a.len + KW - 1) / KW) * a.hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW>), dim3(nblk), dim3(kKvNW * 64), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0>), dim3(nblk), dim3(kKvNW * 64), 0,
+                     st, a);
   return hipGetLastError();
 }
 
