@@ -44,28 +44,6 @@ namespace {
 constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
 constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per SIMD; K rows read from LDS)
 
-// LDS DMA of rows [t0, t0 + ROWS) of a token-major [len][heads][D] bf16 tensor
-// (head offset already applied) into a swizzled [ROWS][D] tile.  Each wave
-// moves ROWS/NW * D*2 bytes, 1 KB per instruction; rows past `len` re-read
-// row len-1 (their contribution is masked by the caller).
-template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(const bf16_storage* base, size_t stride, int t0, int len,
-                                         unsigned char* tile, int wu, int lane) {
-  constexpr int ROWB = D * 2, RPI = 1024 / ROWB, CPR = ROWB / 16;
-  constexpr int NI = ROWS / RPI;  // 1 KB instructions per tile
-  static_assert(NI % NW == 0 || NI < NW, "tile instructions must spread over the waves");
-  constexpr int IPW = (NI + NW - 1) / NW;
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int q = wu * IPW + j;
-    if (NI % NW != 0 && q >= NI) break;  // uniform
-    const int r = q * RPI + lane / CPR, slot = lane % CPR;
-    const int row = min(t0 + r, len - 1);
-    const bf16_storage* src = base + (size_t)row * stride + ((slot ^ swz<D>(r)) * 8);
-    lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tile + q * 1024)));
-  }
-}
-
 }  // namespace
 
 // =================================================================== dK / dV
@@ -105,7 +83,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   }
   if constexpr (KLDS) {  // the workgroup's K rows go to LDS once; waves read their 32 rows as B operands
-    dma_tile<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
+    dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
                              ktile, wu, lane);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -130,8 +108,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     const int hh = it / per_head, qt = qt_lo + it % per_head;
     const int head = g * a.group + hh;
     const int r0 = qt * BR;
-    dma_tile<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.q) + (size_t)head * D, qstride, r0, a.len, st, wu, lane);
-    dma_tile<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.dout) + (size_t)head * D, qstride, r0, a.len,
+    dma_rows<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.q) + (size_t)head * D, qstride, r0, a.len, st, wu, lane);
+    dma_rows<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.dout) + (size_t)head * D, qstride, r0, a.len,
                         st + TILEB, wu, lane);
     // row terms [lse2(BR) | Delta(BR)]: the last waves move 64 dwords each
     constexpr int NRW = (2 * BR + 63) / 64;
@@ -292,8 +270,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
   const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
   const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
   auto issue = [&](int t, unsigned char* st) {
-    dma_tile<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
-    dma_tile<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
+    dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
+    dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
   };
 
   auto tile = [&](int t, const unsigned char* st, auto masked_tag) {

@@ -197,6 +197,28 @@ __device__ __forceinline__ Frag<bf16_storage> row_frag(const unsigned char* tile
   return Frag<bf16_storage>{*reinterpret_cast<const uint4*>(tile + r * (D * 2) + c * 16)};
 }
 
+// LDS DMA of rows [t0, t0 + ROWS) of a token-major [len][heads][D] bf16 tensor
+// (head offset already applied, `stride` elements between rows) into a
+// swizzled [ROWS][D] tile.  The NW waves of the workgroup split the 1 KB
+// instructions; rows past `len` re-read row len-1 (callers mask them).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(const bf16_storage* base, size_t stride, int t0, int len,
+                                         unsigned char* tile, int wu, int lane) {
+  constexpr int ROWB = D * 2, RPI = 1024 / ROWB, CPR = ROWB / 16;
+  constexpr int NI = ROWS / RPI;  // 1 KB instructions per tile
+  static_assert(NI % NW == 0 || NI < NW, "tile instructions must spread over the waves");
+  constexpr int IPW = (NI + NW - 1) / NW;
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int q = wu * IPW + j;
+    if (NI % NW != 0 && q >= NI) break;  // uniform
+    const int r = q * RPI + lane / CPR, slot = lane % CPR;
+    const int row = min(t0 + r, len - 1);
+    const bf16_storage* src = base + (size_t)row * stride + ((slot ^ swz<D>(r)) * 8);
+    lds_dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tile + q * 1024)));
+  }
+}
+
 // XCD-aware work order: the dispatcher deals workgroups round-robin over the
 // 8 XCDs, so consecutive logical tiles (which share K/V) are remapped onto
 // one XCD and its L2.
