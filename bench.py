@@ -47,6 +47,10 @@ def parse():
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a reference kernel of "
                         "known traffic for scaling profiler byte counters)")
+    p.add_argument("--summarize-profiles", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn rocprofv3 CSV output (kernel stats, FETCH_SIZE pass, WRITE_SIZE "
+                        "pass, all taken with --copy-ref-mib) into profiles/traffic.json and print the "
+                        "summary tables")
     return p.parse_args()
 
 
@@ -121,7 +125,8 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    for fname, sha in rec.get("source_sha256", {}).items():
+    for fname in HASHED_SOURCES:
+        sha = rec.get("source_sha256", {}).get(fname)
         src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
         if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
             return None
@@ -132,8 +137,71 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
     return None
 
 
+HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "kcommon.h")
+REF_COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_mib: int):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters read
+    for the reference copy of known size, average per kernel, write profiles/traffic.json
+    (with the kernel sources' hashes) and print markdown tables of both passes."""
+    import collections
+    import csv
+    import hashlib
+    if copy_ref_mib <= 0:
+        sys.exit("--summarize-profiles needs the --copy-ref-mib the counter runs used")
+    ref_kib = copy_ref_mib * 1024.0
+
+    def per_kernel(path):
+        acc, cnt, ref = collections.defaultdict(float), collections.Counter(), []
+        for row in csv.DictReader(open(path)):
+            name = row["Kernel_Name"].split("(")[0].replace("void ", "")
+            val = float(row["Counter_Value"])
+            if REF_COPY_KERNEL in name:
+                ref.append(val)
+                continue
+            acc[name] += val
+            cnt[name] += 1
+        if len(ref) != 1:
+            sys.exit(f"{path}: expected one reference copy dispatch, found {len(ref)}")
+        return {k: (acc[k] / cnt[k], cnt[k]) for k in acc}, ref[0]
+
+    fetch, ref_f = per_kernel(fetch_csv)
+    write, ref_w = per_kernel(write_csv)
+    sf, sw = ref_kib / ref_f, ref_kib / ref_w
+    kernels = {}
+    print(f"Scaling: the {copy_ref_mib} MiB reference copy ({ref_kib:.0f} KiB read + {ref_kib:.0f} KiB "
+          f"written) reads FETCH_SIZE = {ref_f:.0f} KiB and WRITE_SIZE = {ref_w:.0f} KiB, so FETCH_SIZE is "
+          f"scaled by {sf:.3f} and WRITE_SIZE by {sw:.3f}.\n")
+    print("| kernel | dispatches | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | read (MB, scaled) | "
+          "written (MB, scaled) |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(set(fetch) & set(write)):
+        (f, n), (wv, _) = fetch[name], write[name]
+        rb, wb = f * sf * 1024.0, wv * sw * 1024.0
+        kernels[name] = {"read_bytes": rb, "write_bytes": wb}
+        print(f"| `{name}` | {n} | {f:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    csrc = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc")
+    rec = {"kernels": kernels,
+           "source_sha256": {f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+                             for f in HASHED_SOURCES},
+           "note": "HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; "
+                   "stale if any listed source changed"}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    rows = list(csv.DictReader(open(stats_csv)))
+    print("\n| kernel | calls | avg (us) | total (ms) | % of kernel time |")
+    print("|---|---|---|---|---|")
+    for row in rows:
+        print(f"| `{row['Name'][:90]}` | {row['Calls']} | {float(row['AverageNs']) / 1e3:.1f} | "
+              f"{float(row['TotalDurationNs']) / 1e6:.1f} | {row['Percentage']} |")
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.copy_ref_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
               f"in this library", file=sys.stderr)
