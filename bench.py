@@ -249,18 +249,22 @@ def main():
 
     ra.ring_attn_profile_enable(True)
     ra.ring_attn_profile_read()  # discard anything recorded before
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record()
+    evs[0].record()
     for i in range(args.steps):
         step()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = evs[0].elapsed_time(evs[-1])
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     recs, copy_ms, hidden_ms = ra.ring_attn_profile_read()
     ra.ring_attn_profile_enable(False)
     ms_step = ms_total / args.steps
     log(f"[bench] {args.steps} timed step(s): {ms_step:.3f} ms/step")
+    # practical matrix-core ceiling at the clock the card holds under MFMA load (after the timed region)
+    sink = torch.empty((ra.MFMA_RATE_SINK_FLOATS,), dtype=torch.float32, device="cuda")
+    mfma_loop = ra.ring_attn_mfma_rate(20000, sink) if w.dtype == "bf16" else None
 
     fwd_flop, bwd_flop = w.fwd_flop(), (w.bwd_flop() if do_bwd else 0.0)
     step_flop = fwd_flop + bwd_flop
@@ -298,6 +302,9 @@ def main():
                    "ranks": len(w.ranks), "pass": "forward+backward" if do_bwd else "forward",
                    "batch": 1},
         "pct_of_peak": round(100.0 * value / peak, 2),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 3), "step_ms_min": round(step_ms[0], 3),
+        "mfma_loop_tflops": round(mfma_loop, 1) if mfma_loop else None,
+        "pct_of_mfma_loop": round(100.0 * value / mfma_loop, 2) if mfma_loop else None,
         "fwd_tflops": None, "bwd_tflops": None,
         "kernels": kern, "overlap": overlap, "roofline": roofline,
     }

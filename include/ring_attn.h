@@ -180,6 +180,21 @@ const char* ring_attn_last_error(void);
 size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int elem_bytes);
 
 /*
+ * Hand the library caller-owned device memory (on the current device) to use
+ * as the K/V staging instead of its own lazily allocated buffer.  `dev_ptr`
+ * must be 256-byte aligned and stay valid until it is replaced, reset or
+ * ring_attn_shutdown() runs; the library never frees it.  Calls whose shape
+ * needs more than `bytes` (ring_attn_workspace_bytes) return
+ * RA_ERR_INVALID_ARG and enqueue nothing.  (NULL, 0) returns to library-owned
+ * staging.  The call synchronises the device first, so no earlier call still
+ * uses the old buffer, and frees the library's own buffer if it had one.
+ * The backward's row-term buffer (8 bytes per query row and head) stays
+ * library-owned.  Errors: RA_ERR_INVALID_ARG (pointer/size mismatch,
+ * misalignment), RA_ERR_HIP.
+ */
+int ring_attn_set_workspace(void* dev_ptr, size_t bytes);
+
+/*
  * Profiling of the library's own launches (measurement support).  While
  * enabled, the library records HIP events around every attention kernel it
  * launches (on the stream it launches on) and around every staging copy (on
@@ -194,6 +209,19 @@ size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int 
  */
 int ring_attn_profile_enable(int enable);
 int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms);
+
+/*
+ * Matrix-core rate probe (measurement support): runs RA_MFMA_RATE_SINK_FLOATS
+ * workgroups of 8 waves, each wave issuing `iters` rounds of four independent
+ * bf16 32x32x16 MFMAs from registers, on `stream`, and waits for it.  Writes
+ * the achieved dense bf16 TFLOP/s to *tflops: the practical ceiling at the
+ * clock the card sustains under matrix load.  `sink` is caller device memory
+ * of RA_MFMA_RATE_SINK_FLOATS floats that receives one checksum per
+ * workgroup.  Errors: RA_ERR_INVALID_ARG (iters outside [1, 2^24], NULL
+ * pointers), RA_ERR_HIP.
+ */
+#define RA_MFMA_RATE_SINK_FLOATS 1024
+int ring_attn_mfma_rate(int iters, float* sink, double* tflops, ra_stream_t stream);
 
 /* Release every library-owned stream, event and staging buffer (all devices). */
 void ring_attn_shutdown(void);

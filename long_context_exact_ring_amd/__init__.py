@@ -28,7 +28,9 @@ EXPORTED = (
     "ring_attn_fwd", "ring_attn_fwd_f32", "ring_attn_merge", "ring_attn_bwd", "ring_attn_bwd_f32",
     "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
     "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
+    "ring_attn_set_workspace", "ring_attn_mfma_rate",
 )
+MFMA_RATE_SINK_FLOATS = 1024
 
 
 class RingAttnError(RuntimeError):
@@ -66,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_last_error.restype = ctypes.c_char_p
     L.ring_attn_workspace_bytes.argtypes = [i, i, i, i]
     L.ring_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.ring_attn_set_workspace.argtypes = [vp, ctypes.c_size_t]
+    L.ring_attn_set_workspace.restype = i
+    L.ring_attn_mfma_rate.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.ring_attn_mfma_rate.restype = i
     L.ring_attn_profile_enable.argtypes = [i]
     L.ring_attn_profile_enable.restype = i
     L.ring_attn_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
@@ -156,6 +162,18 @@ def ring_attn_bwd_f32(q, k_blocks, v_blocks, out, dout, lse, n_blocks, block_len
 
 def ring_attn_workspace_bytes(block_len, kv_heads, head_dim, elem_bytes) -> int:
     return lib().ring_attn_workspace_bytes(block_len, kv_heads, head_dim, elem_bytes)
+
+
+def ring_attn_set_workspace(dev_ptr, nbytes: int) -> None:
+    """Use caller-owned device memory (an address or a tensor; None with 0 resets) as K/V staging."""
+    _check(lib().ring_attn_set_workspace(_addr(dev_ptr) if dev_ptr is not None else None, int(nbytes)))
+
+
+def ring_attn_mfma_rate(iters: int, sink, stream=None) -> float:
+    """Dense bf16 MFMA TFLOP/s of a register-only loop (sink: >= MFMA_RATE_SINK_FLOATS device floats)."""
+    out = ctypes.c_double()
+    _check(lib().ring_attn_mfma_rate(int(iters), _addr(sink), ctypes.byref(out), _stream(stream)))
+    return out.value
 
 
 def ring_attn_profile_enable(enable: bool) -> int:

@@ -78,5 +78,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 // Pipeline diagnostics: NaN-fill two staging buffers; spin for a bounded number of cycles.
 hipError_t launch_fill_nan(void* a, void* b, size_t bytes, hipStream_t st);
 hipError_t launch_spin(long long cycles, hipStream_t st);
+// `blocks` workgroups of 8 waves; sink receives one float per workgroup
+hipError_t launch_mfma_rate(int iters, float* sink, int blocks, hipStream_t st);
 
 }  // namespace ra

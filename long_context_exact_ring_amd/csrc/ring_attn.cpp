@@ -124,6 +124,7 @@ struct Ctx {
   hipEvent_t ev_copied[2] = {nullptr, nullptr}, ev_done[2] = {nullptr, nullptr};
   void* stage = nullptr;  // [kbuf0 | kbuf1 | vbuf0 | vbuf1]
   size_t stage_cap = 0;
+  bool stage_owned = true;  // false: caller memory from ring_attn_set_workspace
   float* delta = nullptr;
   size_t delta_cap = 0;
 };
@@ -161,6 +162,9 @@ static int get_ctx(Ctx** out) {
 
 static int ensure_stage(Ctx* c, size_t bytes) {
   if (c->stage_cap >= bytes) return RA_OK;
+  if (!c->stage_owned)
+    return fail(RA_ERR_INVALID_ARG, "caller workspace holds %zu bytes, this call needs %zu", c->stage_cap,
+                bytes);
   if (c->stage) {
     RA_HIP(hipDeviceSynchronize());
     RA_HIP(hipFree(c->stage));
@@ -395,6 +399,9 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   Ctx* c = nullptr;
   if ((st = get_ctx(&c)) != RA_OK) return st;
   ++g_prof_call;
+  // staging first: a caller workspace that is too small must fail before anything is enqueued
+  if (ring_schedule(sh.rank, sh.n_blocks, sh.causal).size() > 1 && (st = ensure_stage(c, 4 * sh.kv_bytes())) != RA_OK)
+    return st;
   if ((st = ensure_delta(c, 2 * sh.lse_bytes())) != RA_OK) return st;
   float* lse2 = c->delta + (size_t)sh.block_len * sh.heads;
   {
@@ -543,6 +550,45 @@ int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
   return RA_OK;
 }
 
+int set_workspace(void* ptr, size_t bytes) {
+  if ((ptr == nullptr) != (bytes == 0))
+    return fail(RA_ERR_INVALID_ARG, "workspace pointer and size must be both set or both zero");
+  if ((uintptr_t)ptr % 256 != 0) return fail(RA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::lock_guard<std::mutex> lk(g_mu);
+  Ctx* c = nullptr;
+  int st = get_ctx(&c);
+  if (st != RA_OK) return st;
+  // every call that may still read or fill the old staging must finish first
+  RA_HIP(hipDeviceSynchronize());
+  if (c->stage && c->stage_owned) RA_HIP(hipFree(c->stage));
+  c->stage = ptr;
+  c->stage_cap = bytes;
+  c->stage_owned = (ptr == nullptr);
+  return RA_OK;
+}
+
+int mfma_rate(int iters, float* sink, double* tflops, hipStream_t stream) {
+  if (iters < 1 || iters > (1 << 24)) return fail(RA_ERR_INVALID_ARG, "iters %d outside [1, 2^24]", iters);
+  if (!sink || !tflops) return fail(RA_ERR_INVALID_ARG, "sink and tflops must be non-NULL");
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = launch_mfma_rate(iters / 8 + 1, sink, RA_MFMA_RATE_SINK_FLOATS, stream);  // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, stream);
+  if (e == hipSuccess) e = launch_mfma_rate(iters, sink, RA_MFMA_RATE_SINK_FLOATS, stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(RA_ERR_HIP, "mfma rate probe: %s", hipGetErrorString(e));
+  // 8 waves per workgroup, 4 MFMAs of 32x32x16 (2*16384 flop) per wave and iteration
+  const double flop = (double)RA_MFMA_RATE_SINK_FLOATS * 8.0 * 4.0 * 32768.0 * iters;
+  *tflops = flop / (ms * 1e-3) / 1e12;
+  return RA_OK;
+}
+
 void shutdown_all() {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_ctx.empty()) (void)hipDeviceSynchronize();
@@ -551,7 +597,7 @@ void shutdown_all() {
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(c->device);
     (void)hipDeviceSynchronize();
-    if (c->stage) (void)hipFree(c->stage);
+    if (c->stage && c->stage_owned) (void)hipFree(c->stage);
     if (c->delta) (void)hipFree(c->delta);
     hipEvent_t evs[] = {c->ev_entry, c->ev_side_end, c->ev_copied[0], c->ev_copied[1], c->ev_done[0],
                         c->ev_done[1]};
@@ -660,6 +706,16 @@ const char* ring_attn_last_error(void) { return ra::last_error(); }
 size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int elem_bytes) {
   if (block_len < 1 || kv_heads < 1 || head_dim < 1 || (elem_bytes != 2 && elem_bytes != 4)) return 0;
   return 4 * (size_t)block_len * kv_heads * head_dim * elem_bytes;
+}
+
+int ring_attn_set_workspace(void* dev_ptr, size_t bytes) {
+  ra::clear_error();
+  return ra::set_workspace(dev_ptr, bytes);
+}
+
+int ring_attn_mfma_rate(int iters, float* sink, double* tflops, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::mfma_rate(iters, sink, tflops, (hipStream_t)stream);
 }
 
 int ring_attn_profile_enable(int enable) { return ra::profile_enable(enable); }

@@ -4,6 +4,7 @@ declares, and rejects bad arguments on the host before any HIP call.
 No call here passes validation, so nothing touches a GPU (fake device
 addresses are fine: they are compared, never dereferenced).
 """
+import ctypes
 import os
 import re
 import subprocess
@@ -134,3 +135,19 @@ def test_debug_and_profile_toggles():
     assert ra.ring_attn_profile_enable(False) == ra.RA_OK
     recs, copy_ms, hidden = ra.ring_attn_profile_read()   # nothing recorded: no HIP call needed
     assert copy_ms == 0.0 and hidden == 0.0 and all(v == (0.0, 0) for v in recs.values())
+
+
+def test_set_workspace_validation_before_any_hip_call():
+    L = ra.lib()
+    assert L.ring_attn_set_workspace(None, 4096) == ra.RA_ERR_INVALID_ARG       # size without memory
+    assert L.ring_attn_set_workspace(BASE, 0) == ra.RA_ERR_INVALID_ARG          # memory without size
+    assert L.ring_attn_set_workspace(BASE + 16, 4096) == ra.RA_ERR_INVALID_ARG  # not 256-byte aligned
+    assert b"aligned" in L.ring_attn_last_error()
+
+
+def test_mfma_rate_validation_before_any_hip_call():
+    L = ra.lib()
+    out = ctypes.c_double()
+    assert L.ring_attn_mfma_rate(0, BASE, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG
+    assert L.ring_attn_mfma_rate(1 << 25, BASE, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG
+    assert L.ring_attn_mfma_rate(10, None, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG

@@ -81,3 +81,25 @@ def test_bwd_pipeline_ordering_is_deterministic():
     assert torch.equal(res[0][0], res[1][0])
     for j in range(D):
         assert torch.equal(res[0][1][j], res[1][1][j]) and torch.equal(res[0][2][j], res[1][2][j])
+
+
+def test_bwd_rejects_small_caller_workspace_before_enqueueing():
+    require_gpu()
+    d, h, c, D = 128, 2, 256, 3
+    x = [dev(gen_small(61, (c, h, d), "bf16", 1.0, i), "bf16") for i in range(2 + 2 * D)]
+    q, do = x[0], x[1]
+    kb, vb = x[2:2 + D], x[2 + D:]
+    o, l = ra.fwd(q, kb, vb, causal=False, rank=1)
+    small = torch.empty((1024,), dtype=torch.float32, device="cuda")
+    dq = torch.full((c, h, d), 7.0, device="cuda")
+    dkb = [torch.zeros((c, h, d), device="cuda") for _ in range(D)]
+    dvb = [torch.zeros((c, h, d), device="cuda") for _ in range(D)]
+    try:
+        ra.ring_attn_set_workspace(small, 4096)
+        with pytest.raises(ra.RingAttnError, match="workspace"):
+            ra.bwd(q, kb, vb, o, do, l, causal=False, rank=1, dq=dq, dk_blocks=dkb, dv_blocks=dvb)
+        torch.cuda.synchronize()
+    finally:
+        ra.ring_attn_set_workspace(None, 0)
+    assert bool((dq == 7.0).all())
+    assert all(bool((t == 0).all()) for t in dkb + dvb)

@@ -191,3 +191,47 @@ def test_profile_reports_kernels_and_copies():
     log(f"  profile: {recs} copy_ms={copy_ms:.4f} hidden_ms={hidden:.4f}")
     assert recs["fwd_step"][1] == D and recs["copy"][1] == D - 1
     assert copy_ms > 0 and 0 <= hidden <= copy_ms + 1e-6
+
+
+def test_caller_workspace():
+    """Staging in caller-owned memory gives bit-identical results; a workspace
+    too small for the call is rejected without touching the outputs."""
+    require_gpu()
+    dtype, d, h, c, D = "bf16", 128, 4, 512, 4
+    q, k, v = _inputs(59, dtype, d, h, h, c, D)
+    kb = [dev(k[j * c:(j + 1) * c], dtype) for j in range(D)]
+    vb = [dev(v[j * c:(j + 1) * c], dtype) for j in range(D)]
+    qd = dev(q[3 * c:4 * c], dtype)
+    o0, l0 = ra.fwd(qd, kb, vb, causal=False, rank=3)
+    torch.cuda.synchronize()
+    need = ra.ring_attn_workspace_bytes(c, h, d, 2)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    small = torch.empty((need // 8,), dtype=torch.float32, device="cuda")
+    try:
+        ra.ring_attn_set_workspace(ws, need)
+        o1, l1 = ra.fwd(qd, kb, vb, causal=False, rank=3)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1)
+        assert not torch.isnan(ws).all()  # the staging really went through the caller's memory
+        ra.ring_attn_set_workspace(small, need // 2)
+        o2 = torch.full_like(o0, 7.0)
+        l2 = torch.full_like(l0, 7.0)
+        with pytest.raises(ra.RingAttnError, match="workspace"):
+            ra.fwd(qd, kb, vb, causal=False, rank=3, out=o2, lse=l2)
+        torch.cuda.synchronize()
+        assert bool((o2 == 7.0).all()) and bool((l2 == 7.0).all())
+    finally:
+        ra.ring_attn_set_workspace(None, 0)
+    o3, l3 = ra.fwd(qd, kb, vb, causal=False, rank=3)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o3) and torch.equal(l0, l3)
+
+
+def test_mfma_rate_probe_is_plausible():
+    require_gpu()
+    sink = torch.empty((ra.MFMA_RATE_SINK_FLOATS,), dtype=torch.float32, device="cuda")
+    tf = ra.ring_attn_mfma_rate(2000, sink)
+    torch.cuda.synchronize()
+    log(f"  mfma loop: {tf:.1f} TFLOP/s")
+    assert 300.0 < tf < 2600.0  # below the public dense bf16 figure, far above any scalar path
+    assert torch.isfinite(sink).all()
