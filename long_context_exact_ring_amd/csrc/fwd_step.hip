@@ -28,6 +28,9 @@
 //  * Epilogue: normalise, then overwrite (first round) or merge into the running
 //    (out, lse) in HBM.
 #include "kcommon.h"
+#include <type_traits>
+
+#include "fwd_common.h"
 #include "kernels.h"
 #include "tile_stage.h"
 
@@ -47,61 +50,6 @@ struct FwdCfg {
   static_assert(BC % 32 == 0 && D % 32 == 0, "32x32 MFMA tiles");
 };
 
-// Normalise this lane's query row and write it, or merge it into the running
-// (out, lse) of earlier rounds: lse' = log(e^lse + e^lse_blk),
-// out' = e^(lse - lse') out + e^(lse_blk - lse') O_blk.  m_run is the reference
-// max (log2 units) the block's exponentials were taken against; l_run is this
-// lane's half of the row sum (the other half sits in lane ^ 32).
-template <int D>
-__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16_t (&o)[D / 32], float m_run,
-                                             float l_run, int head, int qi, int hf) {
-  const float l_tot = l_run + swap_halves(l_run);
-  if (qi >= a.len) return;
-  const size_t qstride = (size_t)a.hq * D;
-  float* orow = a.out + (size_t)qi * qstride + (size_t)head * D;
-  float* lsep = a.lse + (size_t)head * a.len + qi;
-  float lse_cur, w_cur, w_old = 0.f;
-  if (l_tot > 0.f) {
-    lse_cur = (m_run + log2f(l_tot)) * kLn2;
-    w_cur = 1.f / l_tot;
-  } else {
-    lse_cur = kNegInf;
-    w_cur = 0.f;
-  }
-  float lse_new = lse_cur;
-  if (!a.first) {
-    const float lse_old = *lsep;
-    const float mxl = fmaxf(lse_old, lse_cur);
-    if (mxl == kNegInf) {
-      lse_new = kNegInf;
-      w_old = 0.f;
-      w_cur = 0.f;
-    } else {
-      const float eo = expf(lse_old - mxl), ec = expf(lse_cur - mxl);
-      const float z = eo + ec;
-      lse_new = mxl + logf(z);
-      w_old = eo / z;
-      w_cur *= ec / z;
-    }
-  }
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float4* dst = reinterpret_cast<float4*>(orow + dt * 32 + j * 8 + hf * 4);
-      float4 r = make_float4(o[dt][4 * j] * w_cur, o[dt][4 * j + 1] * w_cur, o[dt][4 * j + 2] * w_cur,
-                             o[dt][4 * j + 3] * w_cur);
-      if (!a.first) {
-        const float4 old = *dst;
-        r.x += w_old * old.x;
-        r.y += w_old * old.y;
-        r.z += w_old * old.z;
-        r.w += w_old * old.w;
-      }
-      *dst = r;
-    }
-  if (hf == 0) *lsep = lse_new;
-}
 
 #ifndef RA_FWD_WAVES
 #define RA_FWD_WAVES 8
@@ -278,9 +226,34 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
 // ============================================================================
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
+// Per-lane byte offsets of the operand reads within one LDS stage (a K tile
+// then a V tile).  A swizzled row's chunk order repeats every 16 rows, so the
+// reads of other 32-key (K) or 16-key (V) slices differ from these by
+// immediates, and with the stage known at compile time every read is one
+// ds_read with no address arithmetic.
+template <int D>
+struct FwdLdsOffsets {
+  uint32_t k[D / 16];     // row_frag(n, ks, hf) of the K tile
+  uint32_t v[D / 32][2];  // the two transposed reads of tr_frag(dt * 32, kc = 0) of the V tile
+  __device__ __forceinline__ FwdLdsOffsets(int lane, int tileb) {
+    const int n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k[ks] = n * (D * 2) + (((ks * 2 + hf) ^ swz<D>(n)) * 16);
+    const int gq = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int dcol = dt * 32 + (gq & 1) * 16 + 4 * (i16 & 3);
+        const int r = u * 8 + (gq >> 1) * 4 + (i16 >> 2);
+        v[dt][u] = tileb + r * (D * 2) + (((dcol >> 3) ^ swz<D>(r)) * 16) + (dcol & 7) * 2;
+      }
+  }
+};
+
 template <int D, int BC, int NW, int RG, bool MASKED>
-__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned char* kt_lds,
-                                              const unsigned char* vt_lds,
+__device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned char* stage_lds,
+                                              const FwdLdsOffsets<D>& lo,
                                               const Frag<bf16_storage> (&qf)[RG][D / 16],
                                               f32x16_t (&o)[RG][D / 32], float (&m_run)[RG], float (&l_run)[RG],
                                               int t0, int qi0, int n, int hf, int lane) {
@@ -292,7 +265,7 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
     for (int r = 0; r < RG; ++r) s[r][kt] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const Frag<bf16_storage> kf = row_frag<D>(kt_lds, kt * 32 + n, ks, hf);
+      const Frag<bf16_storage> kf{*reinterpret_cast<const uint4*>(stage_lds + kt * 32 * (D * 2) + lo.k[ks])};
 #pragma unroll
       for (int r = 0; r < RG; ++r) mma(s[r][kt], kf, qf[r][ks]);
     }
@@ -309,16 +282,18 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
         for (int i = 0; i < 16; ++i)
           if (kt * 32 + crow(i, hf) > lim) s[r][kt][i] = kNegInf;
     }
-    // row max over this lane's 16*BC/32 keys, then across the two halves
+    // row max over this lane's 16*BC/32 keys
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[r][kt][i], s[r][kt][i + 1]));
-    mx = fmaxf(mx, swap_halves(mx));
-    const float mxs = mx * a.scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mxs > m_run[r] + kRescaleThreshold) != 0) {
-      const float m_new = fmaxf(m_run[r], mxs);
+    // Each half of the wave checks its own 16 keys per row against the shared
+    // reference; only when some row must move it (rare) are the halves'
+    // maxima exchanged, so the common path has no cross-lane traffic.
+    const float mxh = mx * a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mxh > m_run[r] + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_run[r], fmaxf(mxh, swap_halves(mxh)));
       const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[r] - m_new);
       l_run[r] *= alpha;
 #pragma unroll
@@ -347,7 +322,9 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int kc = 0; kc < BC / 16; ++kc) {
-      const Frag<bf16_storage> vf = tr_frag<D>(vt_lds, dt * 32, kc, lane);
+      const uint2 v0 = ds_read_tr16(stage_lds + kc * 16 * (D * 2) + lo.v[dt][0]);
+      const uint2 v1 = ds_read_tr16(stage_lds + kc * 16 * (D * 2) + lo.v[dt][1]);
+      const Frag<bf16_storage> vf{make_uint4(v0.x, v0.y, v1.x, v1.y)};
 #pragma unroll
       for (int r = 0; r < RG; ++r) mma(o[r][dt], vf, pf[r][kc]);
     }
@@ -421,8 +398,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
         const int q = wu * IPW + j;
-        lds_dma16(kbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
-        lds_dma16(vbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
+        lds_dma16_off(kbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
+        lds_dma16_off(vbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
       }
     } else {  // ragged tail: rows past the end re-read the last row (masked later)
 #pragma unroll
@@ -452,14 +429,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   // (diagonal band, ragged tail) take the masked instantiation
   const int wg_first_row = rt * R;
   const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
-  issue(0, smem);
-  int t = 0;
-  for (; t < nfull; ++t) {
+  const FwdLdsOffsets<D> lo(lane, TILEB);
+  // one unmasked tile; ST is its stage when known at compile time (then every
+  // LDS read address is an offset register plus an immediate), else -1
+  auto open_step = [&](int t, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile t has landed
     __syncthreads();                                     // ... and everyone's; the other buffer is free
-    if (t + 1 < ntiles) issue((t + 1) * BC, smem + ((t + 1) & 1) * STAGE);
-    const unsigned char* rd = smem + (t & 1) * STAGE;
-    fwd_bf16_tile<D, BC, NW, RG, false>(a, rd, rd + TILEB, qf, o, m_run, l_run, t * BC, qi, n, hf, lane);
+    const int sc = ST >= 0 ? ST : (t & 1);
+    if (t + 1 < ntiles) issue((t + 1) * BC, smem + (ST >= 0 ? 1 - ST : 1 - sc) * STAGE);
+    fwd_bf16_tile<D, BC, NW, RG, false>(a, smem + sc * STAGE, lo, qf, o, m_run, l_run, t * BC, qi, n, hf, lane);
+  };
+  issue(0, smem);
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    open_step(t, std::integral_constant<int, 0>{});
+    open_step(t + 1, std::integral_constant<int, 1>{});
+  }
+  if (t < nfull) {
+    open_step(t, std::integral_constant<int, 0>{});
+    ++t;
   }
   for (; t < ntiles; ++t) {
     const int t0 = t * BC;
@@ -467,8 +456,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
     __syncthreads();
     if (t + 1 < ntiles) issue(t0 + BC, smem + ((t + 1) & 1) * STAGE);
     if (a.diag && t0 > row0 + 32 * RG - 1) continue;  // wholly above this wave's rows (uniform)
-    const unsigned char* rd = smem + (t & 1) * STAGE;
-    fwd_bf16_tile<D, BC, NW, RG, true>(a, rd, rd + TILEB, qf, o, m_run, l_run, t0, qi, n, hf, lane);
+    fwd_bf16_tile<D, BC, NW, RG, true>(a, smem + (t & 1) * STAGE, lo, qf, o, m_run, l_run, t0, qi, n, hf, lane);
   }
 #pragma unroll
   for (int r = 0; r < RG; ++r) fwd_epilogue<D>(a, o[r], m_run[r], l_run[r], head, qi + 32 * r, hf);
@@ -599,8 +587,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_pp_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
         const int q = wu * IPW + j;
-        lds_dma16(kbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
-        lds_dma16(vbytes + tb + koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
+        lds_dma16_off(kbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
+        lds_dma16_off(vbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
       }
     } else {
 #pragma unroll
@@ -833,6 +821,9 @@ constexpr int kF32Waves = kFwdWaves;
 #ifndef RA_FWD_PP
 #define RA_FWD_PP 0
 #endif
+#ifndef RA_FWD_PIPE
+#define RA_FWD_PIPE 0
+#endif
 #ifndef RA_FWD_RG
 #define RA_FWD_RG 1
 #endif
@@ -859,6 +850,7 @@ static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
+  if (elem_bytes == 2 && RA_FWD_PIPE != 0) return launch_fwd_pipe_bf16(a, head_dim, st);
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_fwd_bf16<64, RA_FWD_BC, kFwdWaves>(a, st);
     if (head_dim == 128) return launch_fwd_bf16<128, RA_FWD_BC, kFwdWaves>(a, st);
@@ -869,6 +861,8 @@ hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipSt
   return hipErrorInvalidValue;
 }
 
-int fwd_waves_per_block() { return kFwdWaves; }
+int fwd_waves_per_block(int elem_bytes) {
+  return (elem_bytes == 2 && RA_FWD_PIPE != 0) ? fwd_pipe_waves_per_block() : kFwdWaves;
+}
 
 }  // namespace ra

@@ -129,6 +129,15 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) 
                : "memory", "m0");
 }
 
+// Same, with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
+// (no per-lane address arithmetic when only the base moves).
+__device__ __forceinline__ void lds_dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // Same, 4 bytes per lane (lane i's dword lands at lds_base + 4*i).
 __device__ __forceinline__ void lds_dma4(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"

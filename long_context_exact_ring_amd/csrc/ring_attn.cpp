@@ -337,7 +337,7 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   if ((st = get_ctx(&c)) != RA_OK) return st;
   ++g_prof_call;
   const int group = sh.heads / sh.kv_heads;
-  const int hpw = heads_per_block(group, fwd_waves_per_block());
+  const int hpw = heads_per_block(group, fwd_waves_per_block(sh.elem_bytes));
   auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
     FwdArgs a{};
     a.q = q;
