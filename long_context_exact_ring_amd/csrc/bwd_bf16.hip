@@ -41,20 +41,24 @@ namespace {
 #ifndef RA_KV_KLDS
 #define RA_KV_KLDS 1
 #endif
+#ifndef RA_KV_LAG
+#define RA_KV_LAG 1
+#endif
 constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
 constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per SIMD; K rows read from LDS)
 
 }  // namespace
 
 // =================================================================== dK / dV
-template <int D, int BR, int NW, bool KLDS>
+template <int D, int BR, int NW, bool KLDS, bool LAG>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BR * ROWB;
   constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
+  constexpr int NB = LAG ? 3 : 2;                 // LDS stages
   constexpr int KTB = KLDS ? NW * 32 * ROWB : 16;  // the workgroup's K rows (KLDS: read from LDS)
   static_assert(BR % 32 == 0 && (BR == 32 || BR % 64 == 0), "row-term DMA covers 64 dwords per wave");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NB * STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char ktile[KTB];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -123,14 +127,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  auto tile = [&](int it, const unsigned char* st, auto masked_tag) {
+  // part12: S = Q K^T and dP = dO V^T of one query tile, then P and dS as bf16
+  // B fragments; false if every row of the tile precedes this wave's keys.
+  // part3: dV^T += dO^T P and dK^T += Q^T dS with the tile's Q/dO read transposed.
+  using BF = Frag<bf16_storage>;
+  auto part12 = [&](int it, const unsigned char* st, auto masked_tag, BF(&pf)[BR / 32][2],
+                    BF(&sf)[BR / 32][2]) -> bool {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int qt = qt_lo + it % per_head;
     const int r0 = qt * BR;
     const unsigned char* qn = st;
     const unsigned char* dn = st + TILEB;
     const float* rt = reinterpret_cast<const float*>(st + 2 * TILEB);
-    if (MASKED && a.diag && key0 > r0 + BR - 1) return;  // every row precedes this wave's keys
+    if (MASKED && a.diag && key0 > r0 + BR - 1) return false;  // every row precedes this wave's keys
 #pragma unroll
     for (int qs = 0; qs < BR / 32; ++qs) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
@@ -165,33 +174,71 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
         float ds8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ds8[e] = dp[c2 * 8 + e];
-        const Frag<bf16_storage> pf = frag_from_f32<bf16_storage>(p + c2 * 8);
-        const Frag<bf16_storage> sf = frag_from_f32<bf16_storage>(ds8);
+        pf[qs][c2] = frag_from_f32<bf16_storage>(p + c2 * 8);
+        sf[qs][c2] = frag_from_f32<bf16_storage>(ds8);
+      }
+    }
+    return true;
+  };
+  auto part3 = [&](const unsigned char* st, const BF(&pf)[BR / 32][2], const BF(&sf)[BR / 32][2]) {
+    const unsigned char* qn = st;
+    const unsigned char* dn = st + TILEB;
+#pragma unroll
+    for (int qs = 0; qs < BR / 32; ++qs)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
         const int kc = qs * 2 + c2;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          mma(dvT[dt], tr_frag<D>(dn, dt * 32, kc, lane), pf);
-          mma(dkT[dt], tr_frag<D>(qn, dt * 32, kc, lane), sf);
+          mma(dvT[dt], tr_frag<D>(dn, dt * 32, kc, lane), pf[qs][c2]);
+          mma(dkT[dt], tr_frag<D>(qn, dt * 32, kc, lane), sf[qs][c2]);
         }
       }
+  };
+
+  // With LAG, the second half of the waves (the second wave on every SIMD)
+  // runs half a tile behind: in the interval of tile it it first finishes
+  // tile it-1 (part3) and then starts tile it (part12), while the first half
+  // runs part12 then part3 of tile it.  The two waves sharing a SIMD are then
+  // in different phases (matrix core vs exponentials) between barriers.  Tile
+  // it-1 must stay in LDS for that interval, hence three stages.
+  // The whole tile loop is instantiated once per role, so the two programs
+  // do not share (and inflate) one register allocation.
+  auto run = [&](auto lag_tag) {
+    constexpr bool LAGGED = decltype(lag_tag)::value;
+    bool prev_active = false;
+    BF pfl[BR / 32][2], sfl[BR / 32][2];
+    int cur = 0;  // stage of tile it
+    auto step = [&](int it, auto masked_tag) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` has landed
+      __syncthreads();                                     // ... everyone's; the stage of tile it-NB+1 is free
+      const int nxt = cur + 1 == NB ? 0 : cur + 1;
+      if (it + 1 < iters) issue(it + 1, smem + nxt * STAGE);
+      const unsigned char* st = smem + cur * STAGE;
+      if constexpr (LAGGED) {
+        if (prev_active) part3(smem + (cur == 0 ? NB - 1 : cur - 1) * STAGE, pfl, sfl);
+        prev_active = part12(it, st, masked_tag, pfl, sfl);
+      } else {
+        BF pf[BR / 32][2], sf[BR / 32][2];
+        if (part12(it, st, masked_tag, pf, sf)) part3(st, pf, sf);
+      }
+      cur = nxt;
+    };
+    if (iters > 0) issue(0, smem);
+    int it = 0;
+    for (int hh = 0; hh < a.group; ++hh) {
+      const int base = hh * per_head - qt_lo;  // it = base + qt
+      for (; it < base + qt_nb; ++it) step(it, std::true_type{});
+      for (; it < base + qt_full; ++it) step(it, std::false_type{});
+      for (; it < base + nqt; ++it) step(it, std::true_type{});
     }
+    if constexpr (LAGGED)
+      if (prev_active) part3(smem + (cur == 0 ? NB - 1 : cur - 1) * STAGE, pfl, sfl);
   };
-
-  auto step = [&](int it, auto masked_tag) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` has landed
-    __syncthreads();                                     // ... everyone's; the other stage is free
-    if (it + 1 < iters) issue(it + 1, smem + ((it + 1) & 1) * STAGE);
-    tile(it, smem + (it & 1) * STAGE, masked_tag);
-  };
-
-  if (iters > 0) issue(0, smem);
-  int it = 0;
-  for (int hh = 0; hh < a.group; ++hh) {
-    const int base = hh * per_head - qt_lo;  // it = base + qt
-    for (; it < base + qt_nb; ++it) step(it, std::true_type{});
-    for (; it < base + qt_full; ++it) step(it, std::false_type{});
-    for (; it < base + nqt; ++it) step(it, std::true_type{});
-  }
+  if (LAG && wu >= NW / 2)
+    run(std::integral_constant<bool, LAG>{});
+  else
+    run(std::false_type{});
 
   if (key >= a.len) return;
   float* dkp = a.dk + (size_t)key * kvstride + (size_t)g * D;
@@ -357,7 +404,8 @@ static hipError_t launch_dkdv_bf16_t(const BwdArgs& a, hipStream_t st) {
   const int KW = kKvNW * 32;
   const int nblk = ((a.len + KW - 1) / KW) * a.hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0>), dim3(nblk), dim3(kKvNW * 64), 0,
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>), dim3(nblk),
+                     dim3(kKvNW * 64), 0,
                      st, a);
   return hipGetLastError();
 }
