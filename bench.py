@@ -88,6 +88,8 @@ def cpu_baseline(w, rows: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    if w.is_decode:
+        return cpu_baseline_decode(w, threads)
     r = max(w.ranks)
     c = w.block_len
     nblk = r + 1 if w.causal else w.n_blocks
@@ -112,6 +114,100 @@ def cpu_baseline(w, rows: int):
             "seconds": dt}
 
 
+def cpu_baseline_decode(w, threads: int):
+    """The fp64 decode oracle on the K/V heads' first query heads (every row, the whole context)."""
+    import numpy as np
+
+    import oracle
+    from workloads import gen_block
+    c, group = w.block_len, w.heads // w.kv_heads
+    heads = [g * group for g in range(min(4, w.kv_heads))]
+    kvh = [h // group for h in heads]
+    k = [gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype)[:, kvh] for j in range(w.n_blocks)]
+    v = [gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype)[:, kvh] for j in range(w.n_blocks)]
+    q = gen_block(w.seed, "q", 0, w.q_len, w.heads, w.head_dim, w.dtype)[:, heads]
+    t0 = time.time()
+    oracle.decode_forward(q, k, v, w.seq_len)
+    dt = time.time() - t0
+    flop = 4.0 * w.head_dim * len(heads) * w.q_len * w.seq_len
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 numpy decode oracle, {w.q_len} query rows x {len(heads)} heads "
+                       f"(one per K/V head) against all {w.seq_len} keys ({dt:.1f}s)"),
+            "seconds": dt}
+
+
+def run_decode(args, w, torch, ra):
+    """Decode workload: one step = one ring_attn_decode call over every block (HBM-bound)."""
+    from workloads import bf16_bits, gen_block
+    c = w.block_len
+
+    def up(x):
+        return torch.from_numpy(bf16_bits(x).view("int16")).view(torch.bfloat16).cuda()
+
+    t0 = time.time()
+    kb = [up(gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype)) for j in range(w.n_blocks)]
+    vb = [up(gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype)) for j in range(w.n_blocks)]
+    q = up(gen_block(w.seed, "q", 0, w.q_len, w.heads, w.head_dim, w.dtype))
+    out = torch.empty((w.q_len, w.heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.heads, w.q_len), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] decode inputs uploaded in {time.time() - t0:.1f}s")
+
+    def step():
+        ra.decode(q, kb, vb, q_pos0=w.seq_len, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.ring_attn_profile_enable(True)
+    ra.ring_attn_profile_read()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms_total = evs[0].elapsed_time(evs[-1])
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    recs, _, _ = ra.ring_attn_profile_read()
+    ra.ring_attn_profile_enable(False)
+    ms_step = ms_total / args.steps
+    flop = w.fwd_flop()
+    value = flop / (ms_step * 1e-3) / 1e12
+    kern = {}
+    for name, (ms, cnt) in recs.items():
+        if cnt:
+            kern[name] = {"launches_per_step": cnt // args.steps, "avg_launch_ms": ms / cnt,
+                          "ms_per_step": ms / args.steps}
+    # algorithmic bytes of one decode step: every K/V byte once, the query rows, out and lse
+    alg_bytes = w.kv_bytes() + w.q_len * w.heads * w.head_dim * (2 + 4) + w.heads * w.q_len * 4
+    dom_ms = kern.get("decode_partial", {}).get("avg_launch_ms")
+    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms else None
+    roofline = {"bound": "hbm", "kernel": "decode_partial", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
+                "traffic": profiled_traffic("decode_partial", w.head_dim, w.dtype),
+                "algorithmic_bytes": alg_bytes}
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": w.seq_len, "n_blocks": w.n_blocks, "block_len": c,
+                   "heads": w.heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim, "q_len": w.q_len,
+                   "pass": "decode", "batch": 1},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4), "step_ms_min": round(step_ms[0], 4),
+        "hbm_gbs_whole_step": round(alg_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "kernels": kern, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, 0)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def profiled_traffic(kind: str, head_dim: int, dtype: str):
     """HBM bytes per dispatch of a kernel from the committed profiler summary, or None.
 
@@ -130,14 +226,15 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
         src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
         if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
             return None
-    pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel"}.get(kind)
+    pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
+               "decode_partial": "decode_partial_kernel"}.get(kind)
     for name, t in rec.get("kernels", {}).items():
-        if pattern and pattern in name and f"<{head_dim}," in name:
+        if pattern and pattern in name and (f"<{head_dim}," in name or f"<{head_dim}>" in name):
             return round(t["read_bytes"] + t["write_bytes"])
     return None
 
 
-HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "kcommon.h")
+HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "decode.hip", "kcommon.h")
 REF_COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -212,6 +309,10 @@ def main():
     from workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if w.is_decode:
+        torch.cuda.set_device(0)
+        run_decode(args, w, torch, ra)
+        return
     do_bwd = w.backward and not args.fwd_only
     torch.cuda.set_device(0)
     qs, kb, vb, dos = build_inputs(w, torch)

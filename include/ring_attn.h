@@ -202,13 +202,45 @@ int ring_attn_set_workspace(void* dev_ptr, size_t bytes);
  * fills, for each kind, the summed duration in milliseconds and the count:
  *   kinds: 0 = forward step kernel, 1 = backward dK/dV kernel,
  *          2 = backward dQ kernel, 3 = backward preprocess kernel,
- *          4 = merge kernel, 5 = staging copy (K+V of one block)
+ *          4 = merge kernel, 5 = staging copy (K+V of one block),
+ *          6 = decode partial kernel, 7 = decode merge kernel
  * and `hidden_ms`, the part of all copy time that overlaps a kernel interval
  * of the same call (copy/compute overlap on the device timeline).
- * `ms` and `count` must hold at least 6 entries.  Reading resets the records.
+ * `ms` and `count` must hold at least 8 entries.  Reading resets the records.
  */
 int ring_attn_profile_enable(int enable);
 int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms);
+
+/*
+ * ring_attn_decode -- long-context decode: a few new query rows against the
+ * whole context held as ring blocks (inference use of the method; the
+ * per-block statistics combine exactly with the merge of §3.1).  Each host
+ * keeps its K/V block; only the few query rows and their per-block partials
+ * move, so the step reads every K/V byte once and is HBM-bound.  On one GPU
+ * all blocks are processed by one split-key launch (one wavefront per K/V
+ * head and key chunk of a block) followed by a log-sum-exp merge of the
+ * partials.
+ *
+ *   q          device, bf16 [q_len][heads][head_dim]; query i sits at global
+ *              position q_pos0 + i
+ *   k_blocks   host array[n_blocks] of device bf16 [block_len][kv_heads][head_dim];
+ *   v_blocks   key t of block j sits at global position j * block_len + t
+ *   n_blocks   1 .. 64;  block_len >= 1;  q_len >= 1;  q_pos0 >= 0
+ *   heads, kv_heads  heads % kv_heads == 0 and (heads / kv_heads) * q_len <= 32
+ *              (RA_ERR_UNSUPPORTED otherwise);  head_dim in {64, 128}
+ *   out        device, fp32 [q_len][heads][head_dim], overwritten
+ *   lse        device, fp32 [heads][q_len] (natural log), overwritten
+ * A key is visible to a query iff its position is <= the query's (q_pos0 >=
+ * n_blocks * block_len - 1 makes every key visible).  A row with no visible
+ * key gets out = 0 and lse = -inf.  out/lse must not overlap each other, q or
+ * any K/V block.  The library keeps a lazily grown device buffer for the
+ * partials (about kv_heads * partials * rows * (head_dim + 1) floats).
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_OOM, RA_ERR_HIP;
+ * nothing is enqueued on error.
+ */
+int ring_attn_decode(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                     int n_blocks, int block_len, int q_len, int heads, int kv_heads, int head_dim,
+                     long long q_pos0, float* out, float* lse, ra_stream_t stream);
 
 /*
  * Matrix-core rate probe (measurement support): runs RA_MFMA_RATE_SINK_FLOATS

@@ -22,13 +22,13 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libringattn.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_OOM = range(5)
-PROFILE_KINDS = ("fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "merge", "copy")
+PROFILE_KINDS = ("fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "merge", "copy", "decode_partial", "decode_merge")
 
 EXPORTED = (
     "ring_attn_fwd", "ring_attn_fwd_f32", "ring_attn_merge", "ring_attn_bwd", "ring_attn_bwd_f32",
     "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
     "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
-    "ring_attn_set_workspace", "ring_attn_mfma_rate",
+    "ring_attn_set_workspace", "ring_attn_mfma_rate", "ring_attn_decode",
 )
 MFMA_RATE_SINK_FLOATS = 1024
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     L.ring_attn_set_workspace.argtypes = [vp, ctypes.c_size_t]
     L.ring_attn_set_workspace.restype = i
+    L.ring_attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_longlong, vp, vp, vp]
+    L.ring_attn_decode.restype = i
     L.ring_attn_mfma_rate.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), vp]
     L.ring_attn_mfma_rate.restype = i
     L.ring_attn_profile_enable.argtypes = [i]
@@ -169,6 +171,12 @@ def ring_attn_set_workspace(dev_ptr, nbytes: int) -> None:
     _check(lib().ring_attn_set_workspace(_addr(dev_ptr) if dev_ptr is not None else None, int(nbytes)))
 
 
+def ring_attn_decode(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0, out,
+                     lse, stream=None) -> int:
+    return lib().ring_attn_decode(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks, block_len, q_len,
+                                  heads, kv_heads, head_dim, int(q_pos0), _addr(out), _addr(lse), _stream(stream))
+
+
 def ring_attn_mfma_rate(iters: int, sink, stream=None) -> float:
     """Dense bf16 MFMA TFLOP/s of a register-only loop (sink: >= MFMA_RATE_SINK_FLOATS device floats)."""
     out = ctypes.c_double()
@@ -182,8 +190,8 @@ def ring_attn_profile_enable(enable: bool) -> int:
 
 def ring_attn_profile_read():
     """Returns ({kind: (ms, count)}, copy_ms, hidden_ms) and resets the records."""
-    ms = (ctypes.c_double * 6)()
-    cnt = (ctypes.c_int * 6)()
+    ms = (ctypes.c_double * len(PROFILE_KINDS))()
+    cnt = (ctypes.c_int * len(PROFILE_KINDS))()
     cms, hid = ctypes.c_double(), ctypes.c_double()
     _check(lib().ring_attn_profile_read(ms, cnt, ctypes.byref(cms), ctypes.byref(hid)))
     return {k: (ms[i], cnt[i]) for i, k in enumerate(PROFILE_KINDS)}, cms.value, hid.value
@@ -246,6 +254,20 @@ def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank
     _check(fn(q, k_blocks, v_blocks, out, dout, lse, len(k_blocks), c, hq, hkv, d, causal, rank, dq,
               dk_blocks, dv_blocks, stream))
     return dq, dk_blocks, dv_blocks
+
+
+def decode(q, k_blocks: List, v_blocks: List, *, q_pos0: int, out=None, lse=None, stream=None):
+    """Decode step: q [q_len, Hq, d] bf16 against every block; returns (out, lse)."""
+    import torch
+    q_len, hq, d = q.shape
+    block_len, hkv = k_blocks[0].shape[0], k_blocks[0].shape[1]
+    if out is None:
+        out = torch.empty((q_len, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((hq, q_len), dtype=torch.float32, device=q.device)
+    _check(ring_attn_decode(q, k_blocks, v_blocks, len(k_blocks), block_len, q_len, hq, hkv, d, q_pos0, out, lse,
+                            stream))
+    return out, lse
 
 
 def merge(out_a, lse_a, out_b, lse_b, *, out=None, lse=None, stream=None):

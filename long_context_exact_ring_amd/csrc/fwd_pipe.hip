@@ -345,6 +345,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
   for (; t < nfull; ++t) body(t, Open{}, std::integral_constant<int, -1>{});
   for (; t < T; ++t) body(t, Masked{}, std::integral_constant<int, -1>{});
   pipe_pv<D>(o[1], vf, p1);  // drain: O_g1 += V(T-1)^T P_g1(T-1)
+  // the clamped copies issued for tiles past the end are still in flight: no
+  // copy into this workgroup's LDS may outlive it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
   for (int r = 0; r < 2; ++r) fwd_epilogue<D>(a, o[r], m_run[r], l_run[r], head, qi[r], hf);

@@ -79,6 +79,26 @@ struct MergeArgs {
 };
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 
+// Decode: q_len query rows against every K/V block, split over key chunks
+// (one wave each), then merged.  Partials: [hkv][n_parts][group*q_len][D]
+// and [hkv][n_parts][group*q_len], n_parts = n_blocks * n_chunks.
+constexpr int kDecodeMaxBlocks = 64;
+struct DecodeArgs {
+  const void* q;                        // [q_len][hq][D] bf16
+  const void* kblk[kDecodeMaxBlocks];   // block j: [len][hkv][D] bf16
+  const void* vblk[kDecodeMaxBlocks];
+  float* out;                           // [q_len][hq][D]
+  float* lse;                           // [hq][q_len]
+  float* part_o;
+  float* part_lse;
+  long long q_pos0;                     // global position of query row 0
+  int n_blocks, len, q_len, hq, hkv, group;
+  int chunk, n_chunks, n_parts;         // keys per wave, chunks per block, partials per row
+  float scale_log2;
+};
+hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
+
 // Pipeline diagnostics: NaN-fill two staging buffers; spin for a bounded number of cycles.
 hipError_t launch_fill_nan(void* a, void* b, size_t bytes, hipStream_t st);
 hipError_t launch_spin(long long cycles, hipStream_t st);

@@ -127,6 +127,8 @@ struct Ctx {
   bool stage_owned = true;  // false: caller memory from ring_attn_set_workspace
   float* delta = nullptr;
   size_t delta_cap = 0;
+  float* dec = nullptr;  // decode partials
+  size_t dec_cap = 0;
 };
 
 static std::mutex g_mu;
@@ -197,6 +199,23 @@ static int ensure_delta(Ctx* c, size_t bytes) {
   return RA_OK;
 }
 
+static int ensure_dec(Ctx* c, size_t bytes) {
+  if (c->dec_cap >= bytes) return RA_OK;
+  if (c->dec) {
+    RA_HIP(hipDeviceSynchronize());
+    RA_HIP(hipFree(c->dec));
+    c->dec = nullptr;
+    c->dec_cap = 0;
+  }
+  if (hipMalloc((void**)&c->dec, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    c->dec = nullptr;
+    return fail(RA_ERR_OOM, "could not allocate %zu bytes for decode partials", bytes);
+  }
+  c->dec_cap = bytes;
+  return RA_OK;
+}
+
 // profiling helpers (only active while enabled)
 static hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -230,7 +249,17 @@ struct ProfScope {
   }
 };
 
-enum { KIND_FWD = 0, KIND_DKDV = 1, KIND_DQ = 2, KIND_PRE = 3, KIND_MERGE = 4, KIND_COPY = 5 };
+enum {
+  KIND_FWD = 0,
+  KIND_DKDV = 1,
+  KIND_DQ = 2,
+  KIND_PRE = 3,
+  KIND_MERGE = 4,
+  KIND_COPY = 5,
+  KIND_DEC_PART = 6,
+  KIND_DEC_MERGE = 7,
+  KIND_COUNT = 8
+};
 
 // ------------------------------------------------------------------ copy engine choice
 static hipMemcpyKind copy_kind() {
@@ -496,7 +525,7 @@ int profile_enable(int on) {
 int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
   if (!ms || !count) return fail(RA_ERR_INVALID_ARG, "profile_read: NULL output array");
   std::lock_guard<std::mutex> lk(g_mu);
-  for (int k = 0; k < 6; ++k) {
+  for (int k = 0; k < KIND_COUNT; ++k) {
     ms[k] = 0.0;
     count[k] = 0;
   }
@@ -550,6 +579,88 @@ int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
   return RA_OK;
 }
 
+#ifndef RA_DEC_WAVES
+#define RA_DEC_WAVES 2048
+#endif
+
+int decode_impl(const void* q, const void* const* kb, const void* const* vb, int n_blocks, int block_len,
+                int q_len, int heads, int kv_heads, int head_dim, long long q_pos0, float* out, float* lse,
+                hipStream_t stream) {
+  if (!q || !out || !lse) return fail(RA_ERR_INVALID_ARG, "q, out and lse must be non-NULL");
+  if (!kb || !vb) return fail(RA_ERR_INVALID_ARG, "k_blocks/v_blocks array is NULL");
+  if (n_blocks < 1 || n_blocks > kDecodeMaxBlocks)
+    return fail(RA_ERR_INVALID_ARG, "n_blocks %d outside [1, %d]", n_blocks, kDecodeMaxBlocks);
+  if (block_len < 1 || q_len < 1) return fail(RA_ERR_INVALID_ARG, "block_len and q_len must be >= 1");
+  if (heads < 1 || kv_heads < 1 || heads % kv_heads != 0)
+    return fail(RA_ERR_INVALID_ARG, "heads (%d) must be a positive multiple of kv_heads (%d)", heads, kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  const int group = heads / kv_heads;
+  if ((long long)group * q_len > 32)
+    return fail(RA_ERR_UNSUPPORTED, "decode takes at most 32 query rows per K/V head (group %d x q_len %d)", group,
+                q_len);
+  if (q_pos0 < 0) return fail(RA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
+  if ((double)block_len * kv_heads * head_dim >= 2147483647.0)
+    return fail(RA_ERR_INVALID_ARG, "block_len*kv_heads*head_dim exceeds 2^31-1");
+  for (int j = 0; j < n_blocks; ++j)
+    if (!kb[j] || !vb[j]) return fail(RA_ERR_INVALID_ARG, "k_blocks[%d] or v_blocks[%d] is NULL", j, j);
+  const size_t qbytes = (size_t)q_len * heads * head_dim * 2, obytes = (size_t)q_len * heads * head_dim * 4,
+               lbytes = (size_t)heads * q_len * 4, kvb = (size_t)block_len * kv_heads * head_dim * 2;
+  if (overlaps(out, obytes, lse, lbytes)) return fail(RA_ERR_INVALID_ARG, "out overlaps lse");
+  const void* outs[2] = {out, lse};
+  const size_t ob[2] = {obytes, lbytes};
+  for (int o = 0; o < 2; ++o) {
+    if (overlaps(outs[o], ob[o], q, qbytes)) return fail(RA_ERR_INVALID_ARG, "%s overlaps q", o ? "lse" : "out");
+    for (int j = 0; j < n_blocks; ++j)
+      if (overlaps(outs[o], ob[o], kb[j], kvb) || overlaps(outs[o], ob[o], vb[j], kvb))
+        return fail(RA_ERR_INVALID_ARG, "%s overlaps K/V block %d", o ? "lse" : "out", j);
+  }
+  // keys per wave: about RA_DEC_WAVES waves over the whole context, 256..8192 keys each
+  const double total = (double)n_blocks * kv_heads * block_len;
+  int chunk = (int)std::min(8192.0, std::max(256.0, std::ceil(total / (double)RA_DEC_WAVES / 32.0) * 32.0));
+  const int n_chunks = (block_len + chunk - 1) / chunk;
+  const int rows = group * q_len;
+  const size_t n_parts = (size_t)n_blocks * n_chunks;
+  const size_t need = (size_t)kv_heads * n_parts * rows * (head_dim + 1) * sizeof(float);
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  Ctx* c = nullptr;
+  int st = get_ctx(&c);
+  if (st != RA_OK) return st;
+  if ((st = ensure_dec(c, need)) != RA_OK) return st;
+  DecodeArgs a{};
+  a.q = q;
+  for (int j = 0; j < n_blocks; ++j) {
+    a.kblk[j] = kb[j];
+    a.vblk[j] = vb[j];
+  }
+  a.out = out;
+  a.lse = lse;
+  a.part_o = c->dec;
+  a.part_lse = c->dec + (size_t)kv_heads * n_parts * rows * head_dim;
+  a.q_pos0 = q_pos0;
+  a.n_blocks = n_blocks;
+  a.len = block_len;
+  a.q_len = q_len;
+  a.hq = heads;
+  a.hkv = kv_heads;
+  a.group = group;
+  a.chunk = chunk;
+  a.n_chunks = n_chunks;
+  a.n_parts = (int)n_parts;
+  a.scale_log2 = 1.4426950408889634f * rsqrt_dim(head_dim);
+  ++g_prof_call;
+  {
+    ProfScope ps(KIND_DEC_PART, stream);
+    RA_HIP(launch_decode_partial(a, head_dim, stream));
+  }
+  {
+    ProfScope ps(KIND_DEC_MERGE, stream);
+    RA_HIP(launch_decode_merge(a, head_dim, stream));
+  }
+  return RA_OK;
+}
+
 int set_workspace(void* ptr, size_t bytes) {
   if ((ptr == nullptr) != (bytes == 0))
     return fail(RA_ERR_INVALID_ARG, "workspace pointer and size must be both set or both zero");
@@ -599,6 +710,7 @@ void shutdown_all() {
     (void)hipDeviceSynchronize();
     if (c->stage && c->stage_owned) (void)hipFree(c->stage);
     if (c->delta) (void)hipFree(c->delta);
+    if (c->dec) (void)hipFree(c->dec);
     hipEvent_t evs[] = {c->ev_entry, c->ev_side_end, c->ev_copied[0], c->ev_copied[1], c->ev_done[0],
                         c->ev_done[1]};
     for (hipEvent_t e : evs)
@@ -711,6 +823,14 @@ size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int 
 int ring_attn_set_workspace(void* dev_ptr, size_t bytes) {
   ra::clear_error();
   return ra::set_workspace(dev_ptr, bytes);
+}
+
+int ring_attn_decode(const void* q, const void* const* k_blocks, const void* const* v_blocks, int n_blocks,
+                     int block_len, int q_len, int heads, int kv_heads, int head_dim, long long q_pos0, float* out,
+                     float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::decode_impl(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0, out,
+                         lse, (hipStream_t)stream);
 }
 
 int ring_attn_mfma_rate(int iters, float* sink, double* tflops, ra_stream_t stream) {

@@ -27,9 +27,11 @@ from .dense import (attention_fwd, attention_bwd, brute_force_fwd, positions_for
                     sampled_rows_fwd)
 from .ring import (ring_steps, simulate_ring, ring_forward, online_block_forward,
                    merge_partials, merge_partials_scalar)
+from .decode import decode_forward, decode_by_partials
 
 __all__ = [
     "attention_fwd", "attention_bwd", "brute_force_fwd", "positions_for_block",
     "sampled_rows_fwd", "ring_steps", "simulate_ring", "ring_forward",
     "online_block_forward", "merge_partials", "merge_partials_scalar",
+    "decode_forward", "decode_by_partials",
 ]

@@ -151,3 +151,26 @@ def test_mfma_rate_validation_before_any_hip_call():
     assert L.ring_attn_mfma_rate(0, BASE, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG
     assert L.ring_attn_mfma_rate(1 << 25, BASE, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG
     assert L.ring_attn_mfma_rate(10, None, ctypes.byref(out), None) == ra.RA_ERR_INVALID_ARG
+
+
+def test_decode_validation_before_any_hip_call():
+    L = ra.lib()
+    q, o, l = BASE, BASE + 0x10000000, BASE + 0x20000000
+    kb = (ctypes.c_void_p * 2)(BASE + 0x30000000, BASE + 0x40000000)
+    vb = (ctypes.c_void_p * 2)(BASE + 0x50000000, BASE + 0x60000000)
+
+    def call(**kw):
+        a = dict(q=q, kb=kb, vb=vb, nb=2, c=256, ql=1, hq=8, hkv=2, d=128, pos=511, o=o, l=l)
+        a.update(kw)
+        return L.ring_attn_decode(a["q"], a["kb"], a["vb"], a["nb"], a["c"], a["ql"], a["hq"], a["hkv"], a["d"],
+                                  a["pos"], a["o"], a["l"], None)
+    assert call(q=None) == ra.RA_ERR_INVALID_ARG
+    assert call(nb=0) == ra.RA_ERR_INVALID_ARG
+    assert call(nb=65) == ra.RA_ERR_INVALID_ARG
+    assert call(ql=0) == ra.RA_ERR_INVALID_ARG
+    assert call(hq=6, hkv=4) == ra.RA_ERR_INVALID_ARG
+    assert call(d=96) == ra.RA_ERR_UNSUPPORTED
+    assert call(ql=9) == ra.RA_ERR_UNSUPPORTED          # group 4 x 9 rows > 32
+    assert call(pos=-1) == ra.RA_ERR_INVALID_ARG
+    assert call(l=o + 16) == ra.RA_ERR_INVALID_ARG       # lse inside out
+    assert call(o=kb[1]) == ra.RA_ERR_INVALID_ARG        # out overlaps a K block

@@ -45,13 +45,25 @@ class Workload:
     backward: bool        # whether the pass includes the backward step
     seed: int
     description: str = ""
+    q_len: int = 0        # decode workloads: new query rows placed after the whole context
 
     @property
     def block_len(self) -> int:
         return self.seq_len // self.n_blocks
 
+    @property
+    def is_decode(self) -> bool:
+        return self.q_len > 0
+
+    def kv_bytes(self) -> int:
+        """Bytes of every K and V block (each read once by a decode step)."""
+        esize = 2 if self.dtype == "bf16" else 4
+        return 2 * self.seq_len * self.kv_heads * self.head_dim * esize
+
     def visible_pairs(self, rank: int) -> int:
-        """Unmasked (query, key) pairs of one rank's share."""
+        """Unmasked (query, key) pairs of one rank's share (decode: every query sees every key)."""
+        if self.is_decode:
+            return self.q_len * self.seq_len
         c = self.block_len
         if not self.causal:
             return c * self.seq_len
@@ -77,6 +89,9 @@ WORKLOADS: Dict[str, Workload] = {
                  "hidden 1024 as 16 heads x 64, one rank against 8 blocks of 8192"),
         Workload("causal_128k_h32_d128", 131072, 16, 32, 32, 128, True, tuple(range(16)), "bf16", True, 3,
                  "causal full sequence, every rank's share, 16 blocks of 8192"),
+        Workload("decode_512k_gqa32x8_q4", 524288, 8, 32, 8, 128, False, (0,), "bf16", False, 6,
+                 "decode: 4 new query rows after a 512k-token context held as 8 blocks of 65536, GQA 32/8",
+                 q_len=4),
         Workload("causal_512k_gqa32x8_rank7", 524288, 8, 32, 8, 128, True, (7,), "bf16", False, 4,
                  "rank 7's share at 512k tokens, GQA 32/8, 8 blocks of 65536"),
         Workload("bwd_causal_32k_h32_d128", 32768, 4, 32, 32, 128, True, (0, 1, 2, 3), "bf16", True, 5,
