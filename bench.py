@@ -92,18 +92,25 @@ def cpu_baseline(w, rows: int):
         return cpu_baseline_decode(w, threads)
     r = max(w.ranks)
     c = w.block_len
-    nblk = r + 1 if w.causal else w.n_blocks
+    nblk = w.n_blocks if (w.zigzag or not w.causal) else r + 1
     k = np.concatenate([gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(nblk)])
     v = np.concatenate([gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(nblk)])
     q = gen_block(w.seed, "q", r, c, w.heads, w.head_dim, w.dtype)
     sel = np.linspace(0, c - 1, rows).astype(np.int64)
-    qpos = r * c + sel
+    if w.zigzag:  # global positions of the zig-zag layout; keys sorted by position
+        qpos = oracle.zigzag_positions(r, w.n_blocks, c)[sel]
+        kpos = np.concatenate([oracle.zigzag_positions(j, w.n_blocks, c) for j in range(nblk)])
+        order = np.argsort(kpos)
+        k, v, kpos = k[order], v[order], kpos[order]
+    else:
+        qpos = r * c + sel
+        kpos = None
     t0 = time.time()
     if w.backward:
         do = gen_block(w.seed, "do", r, c, w.heads, w.head_dim, w.dtype)
-        oracle.attention_bwd(q[sel], k, v, do[sel], causal=w.causal, q_pos=qpos)
+        oracle.attention_bwd(q[sel], k, v, do[sel], causal=w.causal, q_pos=qpos, k_pos=kpos)
     else:
-        oracle.attention_fwd(q[sel], k, v, causal=w.causal, q_pos=qpos)
+        oracle.attention_fwd(q[sel], k, v, causal=w.causal, q_pos=qpos, k_pos=kpos)
     dt = time.time() - t0
     pairs = float(np.sum(qpos + 1)) if w.causal else float(rows * w.seq_len)
     flop = 4.0 * w.head_dim * w.heads * pairs * (3.5 if w.backward else 1.0)
@@ -163,12 +170,18 @@ def run_decode(args, w, torch, ra):
     ra.ring_attn_profile_read()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    timing["on"] = True
     evs[0].record()
     for i in range(args.steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
+    timing["on"] = False
     ms_total = evs[0].elapsed_time(evs[-1])
+    rank_ms = {}
+    for r, marks in rank_ev.items():
+        tot = sum(marks[i][1].elapsed_time(marks[i + 1][1]) for i in range(0, len(marks) - 1, 2))
+        rank_ms[r] = tot / args.steps
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     recs, _, _ = ra.ring_attn_profile_read()
     ra.ring_attn_profile_enable(False)
@@ -324,15 +337,29 @@ def main():
         dkb = [torch.zeros((c, hkv, d), dtype=torch.float32, device="cuda") for _ in range(w.n_blocks)]
         dvb = [torch.zeros((c, hkv, d), dtype=torch.float32, device="cuda") for _ in range(w.n_blocks)]
 
+    # per-rank device time (one rank's forward + backward calls), a load-balance indicator
+    rank_ev = {r: [] for r in w.ranks}
+    timing = {"on": False}
+
+    def mark(r, which):
+        if timing["on"]:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            rank_ev[r].append((which, e))
+
     def step():
         for r in w.ranks:
-            ra.fwd(qs[r], kb, vb, causal=w.causal, rank=r, out=outs[r], lse=lses[r])
+            mark(r, 0)
+            ra.fwd(qs[r], kb, vb, causal=w.causal, rank=r, out=outs[r], lse=lses[r], zigzag=w.zigzag)
+            mark(r, 1)
         if do_bwd:
             for t in dkb + dvb:
                 t.zero_()
             for r in w.ranks:
+                mark(r, 0)
                 ra.bwd(qs[r], kb, vb, outs[r], dos[r], lses[r], causal=w.causal, rank=r, dq=dqs[r],
-                       dk_blocks=dkb, dv_blocks=dvb)
+                       dk_blocks=dkb, dv_blocks=dvb, zigzag=w.zigzag)
+                mark(r, 1)
 
     if args.copy_ref_mib > 0:
         nbytes = args.copy_ref_mib << 20
@@ -352,12 +379,18 @@ def main():
     ra.ring_attn_profile_read()  # discard anything recorded before
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
+    timing["on"] = True
     evs[0].record()
     for i in range(args.steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
+    timing["on"] = False
     ms_total = evs[0].elapsed_time(evs[-1])
+    rank_ms = {}
+    for r, marks in rank_ev.items():
+        tot = sum(marks[i][1].elapsed_time(marks[i + 1][1]) for i in range(0, len(marks) - 1, 2))
+        rank_ms[r] = tot / args.steps
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     recs, copy_ms, hidden_ms = ra.ring_attn_profile_read()
     ra.ring_attn_profile_enable(False)
@@ -408,6 +441,9 @@ def main():
         "pct_of_mfma_loop": round(100.0 * value / mfma_loop, 2) if mfma_loop else None,
         "fwd_tflops": None, "bwd_tflops": None,
         "kernels": kern, "overlap": overlap, "roofline": roofline,
+        "layout": "zigzag" if w.zigzag else "contiguous",
+        "rank_ms": [round(rank_ms[r], 3) for r in w.ranks],
+        "rank_balance": round(sum(rank_ms.values()) / len(rank_ms) / max(rank_ms.values()), 4) if rank_ms else None,
     }
     if "fwd_step" in kern:
         # forward-only rate over the forward kernels' own time

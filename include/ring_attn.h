@@ -150,6 +150,30 @@ int ring_attn_bwd_f32(const float* q, const float* const* k_blocks, const float*
                       ra_stream_t stream);
 
 /*
+ * Zig-zag (load-balanced causal) layout of the same two steps.  The sequence
+ * is cut into 2 * n_blocks chunks of block_len / 2 tokens; block b -- rank b's
+ * query block and K/V block b alike -- holds chunk b in its first half and
+ * chunk 2 * n_blocks - 1 - b in its second half.  With a causal mask every
+ * rank then owns the same amount of work (each ring round pairs one early
+ * and one late chunk), instead of rank r doing r + 1 rounds of the
+ * contiguous layout; the ring visits every block in every rank.  Chunk pairs
+ * are processed as half-size steps: a key chunk later than the query chunk is
+ * skipped, the same chunk is the masked diagonal, an earlier one is full.
+ * Arguments, layouts, ownership and errors are those of ring_attn_fwd and
+ * ring_attn_bwd (bf16), except that block_len must be even
+ * (RA_ERR_INVALID_ARG otherwise) and row i of every per-block tensor sits at
+ * the global position of its chunk.
+ */
+int ring_attn_fwd_zigzag(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                         int n_blocks, int block_len, int heads, int kv_heads, int head_dim,
+                         int causal, int rank, float* out, float* lse, ra_stream_t stream);
+int ring_attn_bwd_zigzag(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                         const float* out, const void* dout, const float* lse,
+                         int n_blocks, int block_len, int heads, int kv_heads, int head_dim,
+                         int causal, int rank, float* dq, float* const* dk_blocks,
+                         float* const* dv_blocks, ra_stream_t stream);
+
+/*
  * The ring order used by ring_attn_fwd/ring_attn_bwd for one rank: writes the
  * sequence-block id of every executed round to steps[0..] (round s uses block
  * (rank - s) mod n_blocks; causal drops blocks j > rank) and returns the number

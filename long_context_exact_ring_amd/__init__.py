@@ -29,6 +29,7 @@ EXPORTED = (
     "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
     "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
     "ring_attn_set_workspace", "ring_attn_mfma_rate", "ring_attn_decode",
+    "ring_attn_fwd_zigzag", "ring_attn_bwd_zigzag",
 )
 MFMA_RATE_SINK_FLOATS = 1024
 
@@ -53,12 +54,12 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, i, f32p = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
     fwd_args = [vp, vp, vp, i, i, i, i, i, i, i, f32p, f32p, vp]
-    for name in ("ring_attn_fwd", "ring_attn_fwd_f32"):
+    for name in ("ring_attn_fwd", "ring_attn_fwd_f32", "ring_attn_fwd_zigzag"):
         fn = getattr(L, name)
         fn.argtypes = fwd_args
         fn.restype = i
     bwd_args = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, vp]
-    for name in ("ring_attn_bwd", "ring_attn_bwd_f32"):
+    for name in ("ring_attn_bwd", "ring_attn_bwd_f32", "ring_attn_bwd_zigzag"):
         fn = getattr(L, name)
         fn.argtypes = bwd_args
         fn.restype = i
@@ -147,6 +148,21 @@ def ring_attn_merge(out_a, lse_a, out_b, lse_b, rows, heads, head_dim, out, lse,
                                  head_dim, _addr(out), _addr(lse), _stream(stream))
 
 
+def ring_attn_fwd_zigzag(q, k_blocks, v_blocks, n_blocks, block_len, heads, kv_heads, head_dim, causal, rank,
+                         out, lse, stream=None) -> int:
+    return lib().ring_attn_fwd_zigzag(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks, block_len,
+                                      heads, kv_heads, head_dim, int(bool(causal)), rank, _addr(out), _addr(lse),
+                                      _stream(stream))
+
+
+def ring_attn_bwd_zigzag(q, k_blocks, v_blocks, out, dout, lse, n_blocks, block_len, heads, kv_heads, head_dim,
+                         causal, rank, dq, dk_blocks, dv_blocks, stream=None) -> int:
+    return lib().ring_attn_bwd_zigzag(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), _addr(out),
+                                      _addr(dout), _addr(lse), n_blocks, block_len, heads, kv_heads, head_dim,
+                                      int(bool(causal)), rank, _addr(dq), _ptr_array(dk_blocks),
+                                      _ptr_array(dv_blocks), _stream(stream))
+
+
 def ring_attn_bwd(q, k_blocks, v_blocks, out, dout, lse, n_blocks, block_len, heads, kv_heads, head_dim,
                   causal, rank, dq, dk_blocks, dv_blocks, stream=None) -> int:
     return lib().ring_attn_bwd(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), _addr(out), _addr(dout),
@@ -224,8 +240,11 @@ def _dims(q, k0) -> Tuple[int, int, int, int]:
     return block_len, heads, kv_heads, head_dim
 
 
-def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None, lse=None, stream=None):
-    """Forward ring step on torch tensors; returns (out fp32 [c,Hq,d], lse fp32 [Hq,c])."""
+def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None, lse=None, stream=None,
+        zigzag: bool = False):
+    """Forward ring step on torch tensors; returns (out fp32 [c,Hq,d], lse fp32 [Hq,c]).
+
+    zigzag=True selects the load-balanced layout (block b holds chunks b and 2D-1-b; bf16 only)."""
     import torch
     c, hq, hkv, d = _dims(q, k_blocks[0])
     if out is None:
@@ -235,12 +254,16 @@ def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None,
     fn = ring_attn_fwd if q.dtype == torch.bfloat16 else ring_attn_fwd_f32
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if zigzag:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("the zig-zag layout takes bf16 inputs")
+        fn = ring_attn_fwd_zigzag
     _check(fn(q, k_blocks, v_blocks, len(k_blocks), c, hq, hkv, d, causal, rank, out, lse, stream))
     return out, lse
 
 
 def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank: int, dq=None,
-        dk_blocks=None, dv_blocks=None, stream=None):
+        dk_blocks=None, dv_blocks=None, stream=None, zigzag: bool = False):
     """Backward ring step; dk/dv blocks are accumulated into (zero-initialised if not given)."""
     import torch
     c, hq, hkv, d = _dims(q, k_blocks[0])
@@ -251,6 +274,10 @@ def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank
     if dv_blocks is None:
         dv_blocks = [torch.zeros((c, hkv, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
     fn = ring_attn_bwd if q.dtype == torch.bfloat16 else ring_attn_bwd_f32
+    if zigzag:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("the zig-zag layout takes bf16 inputs")
+        fn = ring_attn_bwd_zigzag
     _check(fn(q, k_blocks, v_blocks, out, dout, lse, len(k_blocks), c, hq, hkv, d, causal, rank, dq,
               dk_blocks, dv_blocks, stream))
     return dq, dk_blocks, dv_blocks

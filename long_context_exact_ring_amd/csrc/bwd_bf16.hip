@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (k >= 0) {  // uniform
       const int e = k * 64 + lane;
       const int r = min(r0 + (e % BR), a.len - 1);
-      const float* src = (e < BR ? a.lse2 : a.delta) + (size_t)head * a.len + r;
+      const float* src = (e < BR ? a.lse2 : a.delta) + (size_t)head * a.ls + r;
       lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_addr(st + 2 * TILEB + k * 256)));
     }
   };
@@ -306,8 +306,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
       of[ks] = frag_load<bf16_storage>(op + ks * 16);
     }
   }
-  const float lse2 = a.lse2[(size_t)head * a.len + min(qi, a.len - 1)];
-  const float dlt = a.delta[(size_t)head * a.len + min(qi, a.len - 1)];
+  const float lse2 = a.lse2[(size_t)head * a.ls + min(qi, a.len - 1)];
+  const float dlt = a.delta[(size_t)head * a.ls + min(qi, a.len - 1)];
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16_t dqT[D / 32];

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a) {
     const int head = g * a.group + hh;
     const int r = qt * BR + tid;
     if (tid < BR) {
-      lse_r = (r < a.len) ? a.lse[(size_t)head * a.len + r] * kLog2e : 0.f;
-      del_r = (r < a.len) ? a.delta[(size_t)head * a.len + r] : 0.f;
+      lse_r = (r < a.len) ? a.lse[(size_t)head * a.ls + r] * kLog2e : 0.f;
+      del_r = (r < a.len) ? a.delta[(size_t)head * a.ls + r] : 0.f;
     }
   };
   auto lstore = [&](int buf) {
@@ -233,8 +233,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
       of[ks] = (qi < a.len) ? frag_load<T>(op + ks * 16) : frag_zero<T>();
     }
   }
-  const float lse2 = (qi < a.len) ? a.lse[(size_t)head * a.len + qi] * kLog2e : 0.f;
-  const float dlt = (qi < a.len) ? a.delta[(size_t)head * a.len + qi] : 0.f;
+  const float lse2 = (qi < a.len) ? a.lse[(size_t)head * a.ls + qi] * kLog2e : 0.f;
+  const float dlt = (qi < a.len) ? a.delta[(size_t)head * a.ls + qi] : 0.f;
 
   f32x16_t dqT[D / 32];
 #pragma unroll

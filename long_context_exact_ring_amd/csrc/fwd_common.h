@@ -22,7 +22,7 @@ __device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16_t (&
   if (qi >= a.len) return;
   const size_t qstride = (size_t)a.hq * D;
   float* orow = a.out + (size_t)qi * qstride + (size_t)head * D;
-  float* lsep = a.lse + (size_t)head * a.len + qi;
+  float* lsep = a.lse + (size_t)head * a.ls + qi;
   float lse_cur, w_cur, w_old = 0.f;
   if (l_tot > 0.f) {
     lse_cur = (m_run + log2f(l_tot)) * kLn2;

@@ -20,6 +20,7 @@ struct FwdArgs {
   int diag;     // causal diagonal block: key j visible to query i iff j <= i
   int first;    // first round of the ring: write instead of merge
   float scale_log2;  // log2(e) / sqrt(D)
+  int ls;       // elements between heads in lse (len, or more when rows are a slice of a longer block)
 };
 
 hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
@@ -37,6 +38,7 @@ struct BwdPreArgs {
   float* delta;      // [hq][len]  Delta = rowsum(dout * out)
   float* lse2;       // [hq][len]  lse * log2(e)
   int len, hq;
+  int ls;            // elements between heads in lse / delta / lse2
 };
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 
@@ -58,6 +60,7 @@ struct BwdArgs {
   int first;
   float scale;       // 1/sqrt(D)
   float scale_log2;  // log2(e)/sqrt(D)
+  int ls;            // elements between heads in lse / delta / lse2
 };
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);

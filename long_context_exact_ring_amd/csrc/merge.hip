@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) {
-    a.delta[(long)h * a.len + r] = acc;
-    a.lse2[(long)h * a.len + r] = a.lse[(long)h * a.len + r] * kLog2e;
+    a.delta[(long)h * a.ls + r] = acc;
+    a.lse2[(long)h * a.ls + r] = a.lse[(long)h * a.ls + r] * kLog2e;
   }
 }
 

@@ -90,6 +90,8 @@ int validate_common(const Shape& sh, const void* q, const void* const* kb, const
     return fail(RA_ERR_INVALID_ARG, "block_len*heads*head_dim = %.0f exceeds 2^31-1", elems);
   for (int j = 0; j < sh.n_blocks; ++j)
     if (!kb[j] || !vb[j]) return fail(RA_ERR_INVALID_ARG, "k_blocks[%d] or v_blocks[%d] is NULL", j, j);
+  if (sh.zigzag && sh.block_len % 2 != 0)
+    return fail(RA_ERR_INVALID_ARG, "zig-zag layout needs an even block_len (got %d)", sh.block_len);
   return RA_OK;
 }
 
@@ -288,7 +290,7 @@ static bool log_schedule() {
 template <typename StepFn>
 static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* const* vb,
                     hipStream_t stream, StepFn&& step_fn) {
-  const std::vector<int> steps = ring_schedule(sh.rank, sh.n_blocks, sh.causal);
+  const std::vector<int> steps = ring_schedule(sh.rank, sh.n_blocks, sh.schedule_causal());
   const int S = (int)steps.size();
   const size_t kvb = sh.kv_bytes();
   if (log_schedule()) {
@@ -344,6 +346,10 @@ static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* 
 
 static float rsqrt_dim(int d) { return 1.0f / std::sqrt((float)d); }
 
+// Zig-zag layout: block b holds sequence chunks b (first half) and 2D-1-b
+// (second half), so every rank's causal work is the same.
+static int zz_chunk(int block, int half, int n_blocks) { return half == 0 ? block : 2 * n_blocks - 1 - block; }
+
 // Query heads that share one workgroup: the largest common divisor of the group
 // size and the wave count (each wave owns 32 rows of one head).
 static int heads_per_block(int group, int waves) {
@@ -367,24 +373,49 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   ++g_prof_call;
   const int group = sh.heads / sh.kv_heads;
   const int hpw = heads_per_block(group, fwd_waves_per_block(sh.elem_bytes));
+  FwdArgs base{};
+  base.q = q;
+  base.out = out;
+  base.lse = lse;
+  base.len = sh.block_len;
+  base.ls = sh.block_len;
+  base.hq = sh.heads;
+  base.hkv = sh.kv_heads;
+  base.group = group;
+  base.hpw = hpw;
+  base.hsub = group / hpw;
+  base.scale_log2 = 1.4426950408889634f * rsqrt_dim(sh.head_dim);
+  bool first_half[2] = {true, true};
   auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
-    FwdArgs a{};
-    a.q = q;
-    a.k = kp;
-    a.v = vp;
-    a.out = out;
-    a.lse = lse;
-    a.len = sh.block_len;
-    a.hq = sh.heads;
-    a.hkv = sh.kv_heads;
-    a.group = group;
-    a.hpw = hpw;
-    a.hsub = group / hpw;
-    a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
-    a.first = (s == 0) ? 1 : 0;
-    a.scale_log2 = 1.4426950408889634f * rsqrt_dim(sh.head_dim);
-    ProfScope ps(KIND_FWD, stream);
-    RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
+    if (!sh.zigzag) {
+      FwdArgs a = base;
+      a.k = kp;
+      a.v = vp;
+      a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
+      a.first = (s == 0) ? 1 : 0;
+      ProfScope ps(KIND_FWD, stream);
+      RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
+      return RA_OK;
+    }
+    // zig-zag: query half u holds chunk zz_chunk(rank, u), key half v chunk zz_chunk(j, v)
+    const int h = sh.block_len / 2;
+    for (int u = 0; u < 2; ++u)
+      for (int v = 0; v < 2; ++v) {
+        const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
+        if (sh.causal && kc > qc) continue;  // every key of the chunk lies in the queries' future
+        FwdArgs a = base;
+        a.q = static_cast<const char*>(q) + (size_t)u * h * sh.heads * sh.head_dim * sh.elem_bytes;
+        a.out = out + (size_t)u * h * sh.heads * sh.head_dim;
+        a.lse = lse + (size_t)u * h;
+        a.k = static_cast<const char*>(kp) + (size_t)v * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
+        a.v = static_cast<const char*>(vp) + (size_t)v * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
+        a.len = h;
+        a.diag = (sh.causal && kc == qc) ? 1 : 0;
+        a.first = first_half[u] ? 1 : 0;
+        first_half[u] = false;
+        ProfScope ps(KIND_FWD, stream);
+        RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
+      }
     return RA_OK;
   };
   return run_ring(c, sh, kb, vb, stream, step);
@@ -429,12 +460,13 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   if ((st = get_ctx(&c)) != RA_OK) return st;
   ++g_prof_call;
   // staging first: a caller workspace that is too small must fail before anything is enqueued
-  if (ring_schedule(sh.rank, sh.n_blocks, sh.causal).size() > 1 && (st = ensure_stage(c, 4 * sh.kv_bytes())) != RA_OK)
+  if (ring_schedule(sh.rank, sh.n_blocks, sh.schedule_causal()).size() > 1 &&
+      (st = ensure_stage(c, 4 * sh.kv_bytes())) != RA_OK)
     return st;
   if ((st = ensure_delta(c, 2 * sh.lse_bytes())) != RA_OK) return st;
   float* lse2 = c->delta + (size_t)sh.block_len * sh.heads;
   {
-    BwdPreArgs p{dout, out, lse, c->delta, lse2, sh.block_len, sh.heads};
+    BwdPreArgs p{dout, out, lse, c->delta, lse2, sh.block_len, sh.heads, sh.block_len};
     ProfScope ps(KIND_PRE, stream);
     RA_HIP(launch_bwd_pre(p, sh.elem_bytes, sh.head_dim, stream));
   }
@@ -442,28 +474,23 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   const int group = sh.heads / sh.kv_heads;
   const int hpw =
       heads_per_block(group, sh.elem_bytes == 2 ? bwd_bf16_waves_per_block() : bwd_dq_waves_per_block());
-  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
-    BwdArgs a{};
-    a.q = q;
-    a.k = kp;
-    a.v = vp;
-    a.dout = dout;
-    a.lse = lse;
-    a.delta = c->delta;
-    a.lse2 = lse2;
-    a.dq = dq;
-    a.dk = dkb[j];
-    a.dv = dvb[j];
-    a.len = sh.block_len;
-    a.hq = sh.heads;
-    a.hkv = sh.kv_heads;
-    a.group = group;
-    a.hpw = hpw;
-    a.hsub = group / hpw;
-    a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
-    a.first = (s == 0) ? 1 : 0;
-    a.scale = scale;
-    a.scale_log2 = 1.4426950408889634f * scale;
+  BwdArgs base{};
+  base.q = q;
+  base.dout = dout;
+  base.lse = lse;
+  base.delta = c->delta;
+  base.lse2 = lse2;
+  base.dq = dq;
+  base.len = sh.block_len;
+  base.ls = sh.block_len;
+  base.hq = sh.heads;
+  base.hkv = sh.kv_heads;
+  base.group = group;
+  base.hpw = hpw;
+  base.hsub = group / hpw;
+  base.scale = scale;
+  base.scale_log2 = 1.4426950408889634f * scale;
+  auto launch_pair = [&](const BwdArgs& a) -> int {
     {
       ProfScope ps(KIND_DKDV, stream);
       RA_HIP(launch_bwd_dkdv(a, sh.elem_bytes, sh.head_dim, stream));
@@ -472,6 +499,44 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       ProfScope ps(KIND_DQ, stream);
       RA_HIP(launch_bwd_dq(a, sh.elem_bytes, sh.head_dim, stream));
     }
+    return RA_OK;
+  };
+  bool first_half[2] = {true, true};
+  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
+    if (!sh.zigzag) {
+      BwdArgs a = base;
+      a.k = kp;
+      a.v = vp;
+      a.dk = dkb[j];
+      a.dv = dvb[j];
+      a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
+      a.first = (s == 0) ? 1 : 0;
+      return launch_pair(a);
+    }
+    const int h = sh.block_len / 2;
+    const size_t qrow = (size_t)sh.heads * sh.head_dim, krow = (size_t)sh.kv_heads * sh.head_dim;
+    for (int u = 0; u < 2; ++u)
+      for (int v = 0; v < 2; ++v) {
+        const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
+        if (sh.causal && kc > qc) continue;
+        BwdArgs a = base;
+        a.q = static_cast<const char*>(q) + u * h * qrow * sh.elem_bytes;
+        a.dout = static_cast<const char*>(dout) + u * h * qrow * sh.elem_bytes;
+        a.lse = lse + (size_t)u * h;
+        a.delta = c->delta + (size_t)u * h;
+        a.lse2 = lse2 + (size_t)u * h;
+        a.dq = dq + u * h * qrow;
+        a.k = static_cast<const char*>(kp) + v * h * krow * sh.elem_bytes;
+        a.v = static_cast<const char*>(vp) + v * h * krow * sh.elem_bytes;
+        a.dk = dkb[j] + v * h * krow;
+        a.dv = dvb[j] + v * h * krow;
+        a.len = h;
+        a.diag = (sh.causal && kc == qc) ? 1 : 0;
+        a.first = first_half[u] ? 1 : 0;
+        first_half[u] = false;
+        int st2 = launch_pair(a);
+        if (st2 != RA_OK) return st2;
+      }
     return RA_OK;
   };
   return run_ring(c, sh, kb, vb, stream, step);
@@ -793,6 +858,25 @@ int ring_attn_bwd_f32(const float* q, const float* const* k_blocks, const float*
   return ra::bwd_impl(q, (const void* const*)k_blocks, (const void* const*)v_blocks, out, dout, lse,
                       make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 4), dq,
                       dk_blocks, dv_blocks, (hipStream_t)stream);
+}
+
+int ring_attn_fwd_zigzag(const void* q, const void* const* k_blocks, const void* const* v_blocks, int n_blocks,
+                         int block_len, int heads, int kv_heads, int head_dim, int causal, int rank, float* out,
+                         float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  ra::Shape sh = make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 2);
+  sh.zigzag = 1;
+  return ra::fwd_impl(q, k_blocks, v_blocks, sh, out, lse, (hipStream_t)stream);
+}
+
+int ring_attn_bwd_zigzag(const void* q, const void* const* k_blocks, const void* const* v_blocks, const float* out,
+                         const void* dout, const float* lse, int n_blocks, int block_len, int heads, int kv_heads,
+                         int head_dim, int causal, int rank, float* dq, float* const* dk_blocks,
+                         float* const* dv_blocks, ra_stream_t stream) {
+  ra::clear_error();
+  ra::Shape sh = make_shape(n_blocks, block_len, heads, kv_heads, head_dim, causal, rank, 2);
+  sh.zigzag = 1;
+  return ra::bwd_impl(q, k_blocks, v_blocks, out, dout, lse, sh, dq, dk_blocks, dv_blocks, (hipStream_t)stream);
 }
 
 int ring_attn_schedule(int rank, int n_blocks, int causal, int* steps, int max_steps) {

@@ -26,12 +26,12 @@ the definition against the pages' invariants.
 from .dense import (attention_fwd, attention_bwd, brute_force_fwd, positions_for_block,
                     sampled_rows_fwd)
 from .ring import (ring_steps, simulate_ring, ring_forward, online_block_forward,
-                   merge_partials, merge_partials_scalar)
+                   merge_partials, merge_partials_scalar, zigzag_positions, visible_pairs_per_rank)
 from .decode import decode_forward, decode_by_partials
 
 __all__ = [
     "attention_fwd", "attention_bwd", "brute_force_fwd", "positions_for_block",
     "sampled_rows_fwd", "ring_steps", "simulate_ring", "ring_forward",
     "online_block_forward", "merge_partials", "merge_partials_scalar",
-    "decode_forward", "decode_by_partials",
+    "decode_forward", "decode_by_partials", "zigzag_positions", "visible_pairs_per_rank",
 ]

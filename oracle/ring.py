@@ -132,3 +132,28 @@ def merge_partials_scalar(o_a: float, l_a: float, o_b: float, l_b: float) -> Tup
     mx = max(l_a, l_b)
     lse = mx + math.log(math.exp(l_a - mx) + math.exp(l_b - mx))
     return math.exp(l_a - lse) * o_a + math.exp(l_b - lse) * o_b, lse
+
+
+def zigzag_positions(block: int, n_blocks: int, block_len: int) -> np.ndarray:
+    """Global positions of the rows of block ``block`` in the zig-zag layout.
+
+    The sequence is cut into 2D chunks of block_len/2 tokens; block b holds
+    chunk b then chunk 2D-1-b, so that under a causal mask every rank pairs an
+    early and a late chunk (the load-balancing reading of "Ring Attention
+    with Blockwise Transformers for Near-Infinite Context" close-reading
+    notes, §3.5: the per-host work of the plain causal split is uneven).
+    """
+    h = block_len // 2
+    first = np.arange(block * h, (block + 1) * h, dtype=np.int64)
+    late = 2 * n_blocks - 1 - block
+    second = np.arange(late * h, (late + 1) * h, dtype=np.int64)
+    return np.concatenate([first, second])
+
+
+def visible_pairs_per_rank(n_blocks: int, block_len: int, zigzag: bool) -> List[int]:
+    """Causal (query, key) pairs each rank's queries see over the whole ring (brute count)."""
+    pos = [zigzag_positions(b, n_blocks, block_len) if zigzag else
+           np.arange(b * block_len, (b + 1) * block_len, dtype=np.int64) for b in range(n_blocks)]
+    allk = np.sort(np.concatenate(pos))
+    return [int(np.sum(np.searchsorted(allk, p, side="right"))) for p in pos]
+

@@ -174,3 +174,11 @@ def test_decode_validation_before_any_hip_call():
     assert call(pos=-1) == ra.RA_ERR_INVALID_ARG
     assert call(l=o + 16) == ra.RA_ERR_INVALID_ARG       # lse inside out
     assert call(o=kb[1]) == ra.RA_ERR_INVALID_ARG        # out overlaps a K block
+
+
+def test_zigzag_rejects_odd_block_len_before_any_hip_call():
+    L = ra.lib()
+    kb = (ctypes.c_void_p * 2)(BASE + 0x30000000, BASE + 0x40000000)
+    vb = (ctypes.c_void_p * 2)(BASE + 0x50000000, BASE + 0x60000000)
+    rc = L.ring_attn_fwd_zigzag(BASE, kb, vb, 2, 33, 2, 2, 128, 1, 0, BASE + 0x10000000, BASE + 0x20000000, None)
+    assert rc == ra.RA_ERR_INVALID_ARG and b"even" in L.ring_attn_last_error()

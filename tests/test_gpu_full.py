@@ -123,3 +123,29 @@ def test_full_backward_causal_32k():
     compare("dq", dq[:, heads], dq_ref, w.dtype)
     compare("dk", dk[:, heads], dk_ref, w.dtype)
     compare("dv", dv[:, heads], dv_ref, w.dtype)
+
+
+def test_full_causal_128k_zigzag_sampled():
+    """The zig-zag layout at full size: ranks 0 and 15, sampled rows and heads, against
+    dense fp64 attention over every key at its zig-zag position."""
+    require_gpu()
+    w = WORKLOADS["causal_128k_h32_d128_zigzag"]
+    log(f"workload {w.name}")
+    c, D = w.block_len, w.n_blocks
+    kblk, vblk = kv_blocks(w)
+    kb = [up(x, w.dtype) for x in kblk]
+    vb = [up(x, w.dtype) for x in vblk]
+    kpos = np.concatenate([oracle.zigzag_positions(j, D, c) for j in range(D)])
+    order = np.argsort(kpos)
+    heads = [0, 31]
+    k = np.concatenate(kblk)[order][:, heads]
+    v = np.concatenate(vblk)[order][:, heads]
+    for r in (0, 15):
+        q = gen_block(w.seed, "q", r, c, w.heads, w.head_dim, w.dtype)
+        out, lse = ra.fwd(up(q, w.dtype), kb, vb, causal=True, rank=r, zigzag=True)
+        torch.cuda.synchronize()
+        rows = sample_rows(c, seed=r)
+        qpos = oracle.zigzag_positions(r, D, c)[rows]
+        o_ref, l_ref = oracle.sampled_rows_fwd(q[rows][:, heads], qpos, k, v, causal=True, k_pos=kpos[order])
+        compare(f"zigzag rank {r} out", out[torch.from_numpy(rows).cuda()][:, heads], o_ref, w.dtype)
+        compare(f"zigzag rank {r} lse", lse[heads][:, torch.from_numpy(rows).cuda()], l_ref, w.dtype)

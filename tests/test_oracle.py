@@ -343,3 +343,39 @@ def test_backward_single_key_has_zero_dq():
     dq, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, causal=False)
     np.testing.assert_allclose(dq, 0.0, atol=1e-15)
     np.testing.assert_allclose(dv[0], do.sum(axis=0), atol=1e-14)
+
+
+# ------------------------------------------------------------ zig-zag layout
+@pytest.mark.parametrize("D", [1, 2, 4, 8])
+def test_zigzag_positions_partition_the_sequence(D):
+    c = 6
+    pos = np.concatenate([oracle.zigzag_positions(b, D, c) for b in range(D)])
+    assert np.array_equal(np.sort(pos), np.arange(D * c))
+
+
+@pytest.mark.parametrize("D", [2, 4, 16])
+def test_zigzag_balances_causal_work(D):
+    c = 8
+    flat = oracle.visible_pairs_per_rank(D, c, zigzag=False)
+    zz = oracle.visible_pairs_per_rank(D, c, zigzag=True)
+    # contiguous: rank r sees r*c*c + c(c+1)/2 pairs; zig-zag: the same count for every rank
+    assert flat == [r * c * c + c * (c + 1) // 2 for r in range(D)]
+    assert len(set(zz)) == 1 and sum(zz) == sum(flat)
+
+
+def test_zigzag_ring_equals_dense_attention():
+    """Every rank's zig-zag share, computed block by block along the ring with online
+    softmax at the chunks' true positions, equals dense causal attention."""
+    D, c, hq, hkv, d = 4, 6, 2, 1, 4
+    S = D * c
+    q, k, v = qkv(17, S, S, hq, hkv, d)
+    o_ref, l_ref = oracle.attention_fwd(q, k, v, causal=True)
+    for r in range(D):
+        qp = oracle.zigzag_positions(r, D, c)
+        state = None
+        for j in oracle.ring_steps(r, D, causal=False):
+            kp = oracle.zigzag_positions(j, D, c)
+            state = online_block_forward(state, q[qp], k[kp], v[kp], causal=True, q_pos=qp, k_pos=kp)
+        o, l = finish_online(state)
+        np.testing.assert_allclose(o, o_ref[qp], atol=1e-12, rtol=0)
+        np.testing.assert_allclose(l, l_ref[:, qp], atol=1e-12, rtol=0)

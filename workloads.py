@@ -46,6 +46,7 @@ class Workload:
     seed: int
     description: str = ""
     q_len: int = 0        # decode workloads: new query rows placed after the whole context
+    zigzag: bool = False  # block b holds sequence chunks b and 2D-1-b (load-balanced causal layout)
 
     @property
     def block_len(self) -> int:
@@ -89,6 +90,9 @@ WORKLOADS: Dict[str, Workload] = {
                  "hidden 1024 as 16 heads x 64, one rank against 8 blocks of 8192"),
         Workload("causal_128k_h32_d128", 131072, 16, 32, 32, 128, True, tuple(range(16)), "bf16", True, 3,
                  "causal full sequence, every rank's share, 16 blocks of 8192"),
+        Workload("causal_128k_h32_d128_zigzag", 131072, 16, 32, 32, 128, True, tuple(range(16)), "bf16", True, 3,
+                 "the causal 128k workload in the zig-zag layout (chunks b and 31-b of 4096 per block)",
+                 zigzag=True),
         Workload("decode_512k_gqa32x8_q4", 524288, 8, 32, 8, 128, False, (0,), "bf16", False, 6,
                  "decode: 4 new query rows after a 512k-token context held as 8 blocks of 65536, GQA 32/8",
                  q_len=4),
