@@ -143,6 +143,21 @@ def cpu_baseline_decode(w, threads: int):
             "seconds": dt}
 
 
+def reference_copy(args, torch):
+    """One plain device copy of --copy-ref-mib MiB: a kernel of known traffic that scales the
+    profiler's byte counters (FETCH_SIZE / WRITE_SIZE) of the same run."""
+    if args.copy_ref_mib <= 0:
+        return
+    nbytes = args.copy_ref_mib << 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] reference copy: {nbytes} bytes read + {nbytes} bytes written")
+    del src, dst
+
+
 def run_decode(args, w, torch, ra):
     """Decode workload: one step = one ring_attn_decode call over every block (HBM-bound)."""
     from workloads import bf16_bits, gen_block
@@ -163,6 +178,7 @@ def run_decode(args, w, torch, ra):
     def step():
         ra.decode(q, kb, vb, q_pos0=w.seq_len, out=out, lse=lse)
 
+    reference_copy(args, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -170,18 +186,12 @@ def run_decode(args, w, torch, ra):
     ra.ring_attn_profile_read()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    timing["on"] = True
     evs[0].record()
     for i in range(args.steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
-    timing["on"] = False
     ms_total = evs[0].elapsed_time(evs[-1])
-    rank_ms = {}
-    for r, marks in rank_ev.items():
-        tot = sum(marks[i][1].elapsed_time(marks[i + 1][1]) for i in range(0, len(marks) - 1, 2))
-        rank_ms[r] = tot / args.steps
     step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     recs, _, _ = ra.ring_attn_profile_read()
     ra.ring_attn_profile_enable(False)
@@ -225,8 +235,8 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
     """HBM bytes per dispatch of a kernel from the committed profiler summary, or None.
 
     profiles/traffic.json holds FETCH_SIZE/WRITE_SIZE-derived bytes (scaled by a
-    reference copy) together with hashes of the kernel sources they were taken
-    with; any source change since then makes the figure stale (None).
+    reference copy) per kernel, each with hashes of the kernel sources it was
+    taken with; any source change since then makes that figure stale (None).
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -234,16 +244,18 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    for fname in HASHED_SOURCES:
-        sha = rec.get("source_sha256", {}).get(fname)
-        src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
-        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
-            return None
     pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
                "decode_partial": "decode_partial_kernel"}.get(kind)
     for name, t in rec.get("kernels", {}).items():
-        if pattern and pattern in name and (f"<{head_dim}," in name or f"<{head_dim}>" in name):
-            return round(t["read_bytes"] + t["write_bytes"])
+        if not (pattern and pattern in name and (f"<{head_dim}," in name or f"<{head_dim}>" in name)):
+            continue
+        for fname, sha in t.get("source_sha256", {}).items():
+            src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
+            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+                return None  # the kernel changed since its counters were taken
+        if not t.get("source_sha256"):
+            return None
+        return round(t["read_bytes"] + t["write_bytes"])
     return None
 
 
@@ -291,13 +303,18 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
         rb, wb = f * sf * 1024.0, wv * sw * 1024.0
         kernels[name] = {"read_bytes": rb, "write_bytes": wb}
         print(f"| `{name}` | {n} | {f:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    # merge into the committed record; every kernel entry carries the source hashes it was taken with
     csrc = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc")
-    rec = {"kernels": kernels,
-           "source_sha256": {f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
-                             for f in HASHED_SOURCES},
-           "note": "HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; "
-                   "stale if any listed source changed"}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    hashes = {f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest() for f in HASHED_SOURCES}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    known = rec.get("kernels", {})
+    for name, t in kernels.items():
+        known[name] = dict(t, source_sha256=hashes)
+    rec = {"kernels": known,
+           "note": "HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; an entry is "
+                   "stale once any source listed with it has changed"}
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     rows = list(csv.DictReader(open(stats_csv)))
     print("\n| kernel | calls | avg (us) | total (ms) | % of kernel time |")
@@ -361,15 +378,7 @@ def main():
                        dk_blocks=dkb, dv_blocks=dvb, zigzag=w.zigzag)
                 mark(r, 1)
 
-    if args.copy_ref_mib > 0:
-        nbytes = args.copy_ref_mib << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] reference copy: {nbytes} bytes read + {nbytes} bytes written")
-        del src, dst
+    reference_copy(args, torch)
     for i in range(args.warmup):
         step()
     torch.cuda.synchronize()
