@@ -38,8 +38,8 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=3)
-    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="causal_128k_h32_d128")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -143,6 +143,42 @@ def cpu_baseline_decode(w, threads: int):
             "seconds": dt}
 
 
+def read_sclk_mhz():
+    """Current shader clock of GPU 0 from rocm-smi (None when unavailable); never blocks > 15 s."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15)
+    except Exception:
+        return None
+    for line in r.stdout.splitlines():
+        if "sclk" in line and "GPU[0]" in line:
+            m = re.search(r"\((\d+)\s*Mhz\)", line, re.IGNORECASE)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+class ClockSampler:
+    """Samples the shader clock once, `delay` seconds into the timed region (CPU thread)."""
+
+    def __init__(self, delay: float = 2.0):
+        import threading
+        self.mhz = None
+        self._t = threading.Timer(delay, self._run)
+        self._t.daemon = True
+
+    def _run(self):
+        self.mhz = read_sclk_mhz()
+
+    def start(self):
+        self._t.start()
+
+    def join(self):
+        self._t.join(timeout=20)
+        return self.mhz
+
+
 def reference_copy(args, torch):
     """One plain device copy of --copy-ref-mib MiB: a kernel of known traffic that scales the
     profiler's byte counters (FETCH_SIZE / WRITE_SIZE) of the same run."""
@@ -231,6 +267,87 @@ def run_decode(args, w, torch, ra):
     print(json.dumps(result), flush=True)
 
 
+def run_ffn(args, w, torch, ra):
+    """Blockwise feedforward workload: one step = ring_attn_ffn_blockwise over the block's rows."""
+    import numpy as np
+
+    from workloads import bf16_bits, gen_ffn
+    x, w1, b1, w2, b2 = gen_ffn(w)
+
+    def up16(a):
+        return torch.from_numpy(bf16_bits(a).view("int16")).view(torch.bfloat16).cuda()
+
+    xd, w1d, w2d = up16(x), up16(w1), up16(w2)
+    b1d, b2d = torch.from_numpy(b1).cuda(), torch.from_numpy(b2).cuda()
+    y = torch.empty((w.rows, w.hidden), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        ra.ffn_blockwise(xd, w1d, w2d, b1=b1d, b2=b2d, chunk_rows=w.chunk_rows, y=y)
+
+    reference_copy(args, torch)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ra.ring_attn_profile_enable(True)
+    ra.ring_attn_profile_read()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ms_total = evs[0].elapsed_time(evs[-1])
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    recs, _, _ = ra.ring_attn_profile_read()
+    ra.ring_attn_profile_enable(False)
+    ms_step = ms_total / args.steps
+    value = w.flop() / (ms_step * 1e-3) / 1e12
+    kern = {}
+    for name, (ms, cnt) in recs.items():
+        if cnt:
+            per = ms / args.steps
+            kern[name] = {"launches_per_step": cnt // args.steps, "avg_launch_ms": ms / cnt, "ms_per_step": per,
+                          "achieved_tflops": (w.flop() / 2) / (per * 1e-3) / 1e12}
+    dom = max(("ffn_up", "ffn_down"), key=lambda k: kern.get(k, {}).get("ms_per_step", 0.0))
+    achieved = kern.get(dom, {}).get("achieved_tflops")
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
+                "traffic": profiled_traffic(dom, 0, "bf16")}
+    result = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "hidden": w.hidden, "ffn": w.ffn,
+                   "chunk_rows": w.chunk_rows, "pass": "feedforward", "batch": 1},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "step_ms_median": round(step_ms[len(step_ms) // 2], 4), "step_ms_min": round(step_ms[0], 4),
+        "intermediate_bytes": w.chunk_rows * w.ffn * 2,
+        "intermediate_bytes_unblocked": w.rows * w.ffn * 2,
+        "kernels": kern, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        sel = np.linspace(0, w.rows - 1, 4096).astype(np.int64)
+        t0 = time.time()
+        oracle.ffn_forward(x[sel], w1, b1, w2, b2)
+        dt = time.time() - t0
+        result["cpu_baseline"] = {"value": 4.0 * len(sel) * w.hidden * w.ffn / dt / 1e12, "unit": "TFLOP/s",
+                                  "cores": int(threads), "kind": "oracle",
+                                  "sample": f"fp64 numpy feedforward oracle on {len(sel)} of the {w.rows} rows "
+                                            f"({dt:.1f}s)", "seconds": dt}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def profiled_traffic(kind: str, head_dim: int, dtype: str):
     """HBM bytes per dispatch of a kernel from the committed profiler summary, or None.
 
@@ -245,9 +362,12 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
     with open(path) as f:
         rec = json.load(f)
     pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
-               "decode_partial": "decode_partial_kernel"}.get(kind)
+               "decode_partial": "decode_partial_kernel", "ffn_up": "gemm_bt_kernel<true>",
+               "ffn_down": "gemm_bt_kernel<false>"}.get(kind)
     for name, t in rec.get("kernels", {}).items():
-        if not (pattern and pattern in name and (f"<{head_dim}," in name or f"<{head_dim}>" in name)):
+        if not (pattern and pattern in name):
+            continue
+        if kind.startswith(("fwd", "bwd", "decode")) and not (f"<{head_dim}," in name or f"<{head_dim}>" in name):
             continue
         for fname, sha in t.get("source_sha256", {}).items():
             src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
@@ -259,7 +379,7 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
     return None
 
 
-HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "decode.hip", "kcommon.h")
+HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "decode.hip", "ffn.hip", "kcommon.h")
 REF_COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -336,8 +456,12 @@ def main():
     import torch
 
     import long_context_exact_ring_amd as ra
-    from workloads import WORKLOADS
+    from workloads import FFN_WORKLOADS, WORKLOADS
 
+    if args.workload in FFN_WORKLOADS:
+        torch.cuda.set_device(0)
+        run_ffn(args, FFN_WORKLOADS[args.workload], torch, ra)
+        return
     w = WORKLOADS[args.workload]
     if w.is_decode:
         torch.cuda.set_device(0)
@@ -389,12 +513,15 @@ def main():
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     timing["on"] = True
+    clock = ClockSampler(min(2.0, 0.3 * args.steps))
+    clock.start()
     evs[0].record()
     for i in range(args.steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
     timing["on"] = False
+    sclk = clock.join()
     ms_total = evs[0].elapsed_time(evs[-1])
     rank_ms = {}
     for r, marks in rank_ev.items():
@@ -447,6 +574,8 @@ def main():
         "pct_of_peak": round(100.0 * value / peak, 2),
         "step_ms_median": round(step_ms[len(step_ms) // 2], 3), "step_ms_min": round(step_ms[0], 3),
         "mfma_loop_tflops": round(mfma_loop, 1) if mfma_loop else None,
+        "sclk_mhz_during_run": sclk,
+        "peak_at_sclk_tflops": round(256 * 4096 * sclk * 1e6 / 1e12, 1) if sclk else None,
         "pct_of_mfma_loop": round(100.0 * value / mfma_loop, 2) if mfma_loop else None,
         "fwd_tflops": None, "bwd_tflops": None,
         "kernels": kern, "overlap": overlap, "roofline": roofline,

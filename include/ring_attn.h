@@ -227,10 +227,11 @@ int ring_attn_set_workspace(void* dev_ptr, size_t bytes);
  *   kinds: 0 = forward step kernel, 1 = backward dK/dV kernel,
  *          2 = backward dQ kernel, 3 = backward preprocess kernel,
  *          4 = merge kernel, 5 = staging copy (K+V of one block),
- *          6 = decode partial kernel, 7 = decode merge kernel
+ *          6 = decode partial kernel, 7 = decode merge kernel,
+ *          8 = feedforward up-projection GEMM, 9 = down-projection GEMM
  * and `hidden_ms`, the part of all copy time that overlaps a kernel interval
  * of the same call (copy/compute overlap on the device timeline).
- * `ms` and `count` must hold at least 8 entries.  Reading resets the records.
+ * `ms` and `count` must hold at least 10 entries.  Reading resets the records.
  */
 int ring_attn_profile_enable(int enable);
 int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms);
@@ -265,6 +266,31 @@ int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidd
 int ring_attn_decode(const void* q, const void* const* k_blocks, const void* const* v_blocks,
                      int n_blocks, int block_len, int q_len, int heads, int kv_heads, int head_dim,
                      long long q_pos0, float* out, float* lse, ra_stream_t stream);
+
+/*
+ * ring_attn_ffn_blockwise -- the feedforward half of a blockwise transformer
+ * layer, computed block by block ("Ring Attention with Blockwise Transformers
+ * for Near-Infinite Context" close-reading notes, §2.2: computing the
+ * feedforward in blocks caps its largest activation at one block of the
+ * 4h-wide intermediate rather than the whole sequence's):
+ *
+ *   y = GELU(x W1^T + b1) W2^T + b2        GELU(z) = z * Phi(z) (exact, erf form)
+ *
+ *   x    device bf16 [rows][hidden]     (e.g. a rank's attention block, rows = block_len)
+ *   w1   device bf16 [ffn][hidden]      w2  device bf16 [hidden][ffn]   (weights [out][in])
+ *   b1   device fp32 [ffn] or NULL      b2  device fp32 [hidden] or NULL
+ *   y    device fp32 [rows][hidden], overwritten; must not overlap any input
+ *   chunk_rows  rows per block (0 = all rows at once).  The library keeps one
+ *        bf16 [chunk_rows][ffn] intermediate, rounds GELU's output to bf16
+ *        there, and runs two MFMA GEMMs per chunk on `stream`.
+ * hidden and ffn must be positive multiples of 128 (RA_ERR_UNSUPPORTED);
+ * rows >= 1; operands must stay under 4 GiB each (RA_ERR_INVALID_ARG).
+ * Errors: RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_OOM, RA_ERR_HIP;
+ * nothing is enqueued on error.
+ */
+int ring_attn_ffn_blockwise(const void* x, const void* w1, const float* b1, const void* w2,
+                            const float* b2, int rows, int hidden, int ffn, int chunk_rows,
+                            float* y, ra_stream_t stream);
 
 /*
  * Matrix-core rate probe (measurement support): runs RA_MFMA_RATE_SINK_FLOATS

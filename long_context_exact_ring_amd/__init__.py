@@ -22,14 +22,15 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libringattn.so")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_OOM = range(5)
-PROFILE_KINDS = ("fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "merge", "copy", "decode_partial", "decode_merge")
+PROFILE_KINDS = ("fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "merge", "copy", "decode_partial", "decode_merge",
+                 "ffn_up", "ffn_down")
 
 EXPORTED = (
     "ring_attn_fwd", "ring_attn_fwd_f32", "ring_attn_merge", "ring_attn_bwd", "ring_attn_bwd_f32",
     "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
     "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
     "ring_attn_set_workspace", "ring_attn_mfma_rate", "ring_attn_decode",
-    "ring_attn_fwd_zigzag", "ring_attn_bwd_zigzag",
+    "ring_attn_fwd_zigzag", "ring_attn_bwd_zigzag", "ring_attn_ffn_blockwise",
 )
 MFMA_RATE_SINK_FLOATS = 1024
 
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_set_workspace.restype = i
     L.ring_attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_longlong, vp, vp, vp]
     L.ring_attn_decode.restype = i
+    L.ring_attn_ffn_blockwise.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
+    L.ring_attn_ffn_blockwise.restype = i
     L.ring_attn_mfma_rate.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), vp]
     L.ring_attn_mfma_rate.restype = i
     L.ring_attn_profile_enable.argtypes = [i]
@@ -193,6 +196,11 @@ def ring_attn_decode(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, k
                                   heads, kv_heads, head_dim, int(q_pos0), _addr(out), _addr(lse), _stream(stream))
 
 
+def ring_attn_ffn_blockwise(x, w1, b1, w2, b2, rows, hidden, ffn, chunk_rows, y, stream=None) -> int:
+    return lib().ring_attn_ffn_blockwise(_addr(x), _addr(w1), _addr(b1), _addr(w2), _addr(b2), rows, hidden, ffn,
+                                         chunk_rows, _addr(y), _stream(stream))
+
+
 def ring_attn_mfma_rate(iters: int, sink, stream=None) -> float:
     """Dense bf16 MFMA TFLOP/s of a register-only loop (sink: >= MFMA_RATE_SINK_FLOATS device floats)."""
     out = ctypes.c_double()
@@ -295,6 +303,17 @@ def decode(q, k_blocks: List, v_blocks: List, *, q_pos0: int, out=None, lse=None
     _check(ring_attn_decode(q, k_blocks, v_blocks, len(k_blocks), block_len, q_len, hq, hkv, d, q_pos0, out, lse,
                             stream))
     return out, lse
+
+
+def ffn_blockwise(x, w1, w2, *, b1=None, b2=None, chunk_rows: int = 0, y=None, stream=None):
+    """y = GELU(x W1^T + b1) W2^T + b2 over row chunks; x [rows, hidden] bf16, weights [out, in] bf16."""
+    import torch
+    rows, hidden = x.shape
+    ffn = w1.shape[0]
+    if y is None:
+        y = torch.empty((rows, hidden), dtype=torch.float32, device=x.device)
+    _check(ring_attn_ffn_blockwise(x, w1, b1, w2, b2, rows, hidden, ffn, chunk_rows, y, stream))
+    return y
 
 
 def merge(out_a, lse_a, out_b, lse_b, *, out=None, lse=None, stream=None):

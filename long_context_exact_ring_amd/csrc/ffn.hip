@@ -1,0 +1,151 @@
+// Blockwise feedforward for gfx950 (the feedforward half of a blockwise
+// transformer layer: "Ring Attention with Blockwise Transformers for
+// Near-Infinite Context" close-reading notes, §2.2 -- computing the
+// feedforward block by block caps its largest activation at the size of one
+// block of the 4h-wide intermediate instead of the whole sequence's).
+//
+//   Y = GELU(X W1^T + b1) W2^T + b2      X [rows][hidden], W1 [ffn][hidden],
+//                                        W2 [hidden][ffn] (weights [out][in])
+//
+// computed over row chunks: per chunk, one GEMM writes the bf16 intermediate
+// H = GELU(X W1^T + b1) of that chunk only, a second GEMM reads it back.
+//
+// GEMM kernel (gemm_bt_kernel): C[m][n] = sum_k A[m][k] B[n][k] with both
+// operands k-contiguous.  A 128x128 workgroup tile, four waves of 64x64, a
+// k-step of 64 staged global -> LDS by LDS DMA into swizzled 128-byte rows
+// (double-buffered, one barrier per k-step).  The MFMA computes the tile
+// transposed (weights as the A operand, activation rows as B), so a lane ends
+// up holding four consecutive output columns of one row: bias, GELU and the
+// bf16 / fp32 stores work on contiguous 8- or 16-byte pieces.
+#include "kcommon.h"
+#include "kernels.h"
+
+namespace ra {
+
+namespace {
+
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 64;
+
+// exact GELU, x * Phi(x), with the error function of the device math library
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.f + erff(x * 0.70710678118654752f)); }
+
+}  // namespace
+
+template <bool GELU_BF16_OUT>
+__global__ __launch_bounds__(256) void gemm_bt_kernel(GemmArgs a) {
+  constexpr int ROWB = kGemmBK * 2;              // 128 bytes per tile row
+  constexpr int TILEB = kGemmBM * ROWB;          // 16 KB per operand tile
+  constexpr int STAGE = 2 * TILEB;               // activation tile, weight tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wu & 1, wn = wu >> 1;  // this wave's 64x64 quadrant
+
+  // workgroup -> (row tile, column tile); consecutive workgroups share the
+  // activation rows (column tiles vary fastest within an XCD's share)
+  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ntn = a.n / kGemmBN;
+  const int tn = logical % ntn, tm = logical / ntn;
+  const int m0 = tm * kGemmBM, n0 = tn * kGemmBN;
+
+  // DMA lane offsets: a 1 KB instruction moves 8 rows of 128 bytes
+  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16;  // 8 rows, 8 chunks per row
+  constexpr int NI = kGemmBM / RPI;                  // 16 instructions per operand tile
+  constexpr int IPW = NI / 4;                        // 4 per wave
+  uint32_t aoff[IPW], boff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wu * IPW + j) * RPI + lane / CPR, slot = lane % CPR;
+    const int mr = min(m0 + r, a.m - 1);  // rows past the end re-read the last row (never stored)
+    aoff[j] = (uint32_t)(((size_t)mr * a.lda + (slot ^ swz<64>(r)) * 8) * 2);
+    boff[j] = (uint32_t)(((size_t)(n0 + r) * a.ldb + (slot ^ swz<64>(r)) * 8) * 2);
+  }
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.a);
+  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(a.b);
+  auto issue = [&](int ks, unsigned char* st) {
+    const size_t kb = (size_t)ks * kGemmBK * 2;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const uint32_t q = (uint32_t)(wu * IPW + j) * 1024;
+      lds_dma16_off(abase + kb, aoff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + q)));
+      lds_dma16_off(bbase + kb, boff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + TILEB + q)));
+    }
+  };
+
+  f32x16_t acc[2][2];  // [weight-row tile][activation-row tile], transposed 32x32 tiles
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = a.k / kGemmBK;
+  issue(0, smem);
+  for (int ks = 0; ks < nk; ++ks) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of k-step ks has landed
+    __syncthreads();                                     // ... everyone's; the other stage is free
+    if (ks + 1 < nk) issue(ks + 1, smem + ((ks + 1) & 1) * STAGE);
+    const unsigned char* at = smem + (ks & 1) * STAGE;  // activation rows
+    const unsigned char* bt = at + TILEB;               // weight rows
+#pragma unroll
+    for (int kk = 0; kk < kGemmBK / 16; ++kk) {
+      Frag<bf16_storage> wf[2], xf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        wf[i] = row_frag<64>(bt, wn * 64 + i * 32 + n, kk, hf);
+        xf[i] = row_frag<64>(at, wm * 64 + i * 32 + n, kk, hf);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma(acc[i][j], wf[i], xf[j]);
+    }
+  }
+
+  // epilogue: lane holds output row m = m0 + wm*64 + j*32 + n and columns
+  // n0 + wn*64 + i*32 + crow(r, hf) for the 16 accumulator registers r
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + wm * 64 + j * 32 + n;
+    if (m >= a.m) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = n0 + wn * 64 + i * 32 + q4 * 8 + hf * 4;  // four consecutive columns
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * q4 + e];
+          if (a.bias) v[e] += a.bias[c0 + e];
+        }
+        if constexpr (GELU_BF16_OUT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
+          f32x2_t lo = {v[0], v[1]}, hi = {v[2], v[3]};
+          const uint2 packed = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                                          __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_storage*>(a.c) + (size_t)m * a.ldc + c0) = packed;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.c) + (size_t)m * a.ldc + c0) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+  }
+}
+
+hipError_t launch_gemm_bt(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st) {
+  if (a.m < 1 || a.n % kGemmBN != 0 || a.k % kGemmBK != 0 || a.n < kGemmBN || a.k < kGemmBK)
+    return hipErrorInvalidValue;
+  const long nblk = (long)((a.m + kGemmBM - 1) / kGemmBM) * (a.n / kGemmBN);
+  if (gelu_bf16_out)
+    hipLaunchKernelGGL(gemm_bt_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(gemm_bt_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+int gemm_tile_n() { return kGemmBN; }
+int gemm_tile_k() { return kGemmBK; }
+
+}  // namespace ra

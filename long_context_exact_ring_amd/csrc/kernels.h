@@ -100,6 +100,19 @@ struct DecodeArgs {
   float scale_log2;
 };
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, hipStream_t st);
+
+// C[m][n] = sum_k A[m][k] B[n][k] (+ bias[n]); bf16 A and B (k contiguous), fp32 accumulation.
+// gelu_bf16_out: C = bf16(GELU(.)) else C = fp32.  n % 128 == 0, k % 64 == 0.
+struct GemmArgs {
+  const void* a;      // [m][lda] bf16
+  const void* b;      // [n][ldb] bf16
+  void* c;            // [m][ldc] bf16 or fp32
+  const float* bias;  // [n] or nullptr
+  int m, n, k, lda, ldb, ldc;
+};
+hipError_t launch_gemm_bt(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st);
+int gemm_tile_n();
+int gemm_tile_k();
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
 
 // Pipeline diagnostics: NaN-fill two staging buffers; spin for a bounded number of cycles.

@@ -131,6 +131,8 @@ struct Ctx {
   size_t delta_cap = 0;
   float* dec = nullptr;  // decode partials
   size_t dec_cap = 0;
+  void* ffn = nullptr;   // blockwise feedforward intermediate (one row chunk)
+  size_t ffn_cap = 0;
 };
 
 static std::mutex g_mu;
@@ -218,6 +220,23 @@ static int ensure_dec(Ctx* c, size_t bytes) {
   return RA_OK;
 }
 
+static int ensure_ffn(Ctx* c, size_t bytes) {
+  if (c->ffn_cap >= bytes) return RA_OK;
+  if (c->ffn) {
+    RA_HIP(hipDeviceSynchronize());
+    RA_HIP(hipFree(c->ffn));
+    c->ffn = nullptr;
+    c->ffn_cap = 0;
+  }
+  if (hipMalloc(&c->ffn, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    c->ffn = nullptr;
+    return fail(RA_ERR_OOM, "could not allocate %zu bytes for the feedforward intermediate", bytes);
+  }
+  c->ffn_cap = bytes;
+  return RA_OK;
+}
+
 // profiling helpers (only active while enabled)
 static hipEvent_t prof_event() {
   if (!g_prof_pool.empty()) {
@@ -260,7 +279,9 @@ enum {
   KIND_COPY = 5,
   KIND_DEC_PART = 6,
   KIND_DEC_MERGE = 7,
-  KIND_COUNT = 8
+  KIND_FFN_UP = 8,
+  KIND_FFN_DOWN = 9,
+  KIND_COUNT = 10
 };
 
 // ------------------------------------------------------------------ copy engine choice
@@ -726,6 +747,48 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   return RA_OK;
 }
 
+int ffn_impl(const void* x, const void* w1, const float* b1, const void* w2, const float* b2, int rows, int hidden,
+             int ffn, int chunk_rows, float* y, hipStream_t stream) {
+  if (!x || !w1 || !w2 || !y) return fail(RA_ERR_INVALID_ARG, "x, w1, w2 and y must be non-NULL");
+  if (rows < 1) return fail(RA_ERR_INVALID_ARG, "rows must be >= 1 (got %d)", rows);
+  const int tn = gemm_tile_n();
+  if (hidden < tn || ffn < tn || hidden % tn != 0 || ffn % tn != 0)
+    return fail(RA_ERR_UNSUPPORTED, "hidden (%d) and ffn (%d) must be positive multiples of %d", hidden, ffn, tn);
+  if (chunk_rows < 0) return fail(RA_ERR_INVALID_ARG, "chunk_rows must be >= 0 (0: all rows at once)");
+  const int chunk = (chunk_rows == 0 || chunk_rows > rows) ? rows : chunk_rows;
+  // byte offsets inside one operand are 32-bit in the kernel
+  const double lim = 4294967295.0;
+  if ((double)rows * hidden * 4 >= lim || (double)chunk * ffn * 2 >= lim || (double)ffn * hidden * 2 >= lim)
+    return fail(RA_ERR_INVALID_ARG, "operand larger than 4 GiB (rows %d, hidden %d, ffn %d)", rows, hidden, ffn);
+  const size_t xb = (size_t)rows * hidden * 2, yb = (size_t)rows * hidden * 4, wb = (size_t)ffn * hidden * 2;
+  const void* ins[] = {x, w1, w2, b1, b2};
+  const size_t inb[] = {xb, wb, wb, (size_t)ffn * 4, (size_t)hidden * 4};
+  for (int i = 0; i < 5; ++i)
+    if (ins[i] && overlaps(y, yb, ins[i], inb[i])) return fail(RA_ERR_INVALID_ARG, "y overlaps an input");
+
+  std::lock_guard<std::mutex> lk(g_mu);
+  Ctx* c = nullptr;
+  int st = get_ctx(&c);
+  if (st != RA_OK) return st;
+  if ((st = ensure_ffn(c, (size_t)chunk * ffn * 2)) != RA_OK) return st;
+  ++g_prof_call;
+  for (int r0 = 0; r0 < rows; r0 += chunk) {
+    const int m = std::min(chunk, rows - r0);
+    GemmArgs up{static_cast<const char*>(x) + (size_t)r0 * hidden * 2, w1, c->ffn, b1, m, ffn, hidden, hidden, hidden,
+                ffn};
+    {
+      ProfScope ps(KIND_FFN_UP, stream);
+      RA_HIP(launch_gemm_bt(up, true, stream));
+    }
+    GemmArgs down{c->ffn, w2, y + (size_t)r0 * hidden, b2, m, hidden, ffn, ffn, ffn, hidden};
+    {
+      ProfScope ps(KIND_FFN_DOWN, stream);
+      RA_HIP(launch_gemm_bt(down, false, stream));
+    }
+  }
+  return RA_OK;
+}
+
 int set_workspace(void* ptr, size_t bytes) {
   if ((ptr == nullptr) != (bytes == 0))
     return fail(RA_ERR_INVALID_ARG, "workspace pointer and size must be both set or both zero");
@@ -776,6 +839,7 @@ void shutdown_all() {
     if (c->stage && c->stage_owned) (void)hipFree(c->stage);
     if (c->delta) (void)hipFree(c->delta);
     if (c->dec) (void)hipFree(c->dec);
+    if (c->ffn) (void)hipFree(c->ffn);
     hipEvent_t evs[] = {c->ev_entry, c->ev_side_end, c->ev_copied[0], c->ev_copied[1], c->ev_done[0],
                         c->ev_done[1]};
     for (hipEvent_t e : evs)
@@ -915,6 +979,12 @@ int ring_attn_decode(const void* q, const void* const* k_blocks, const void* con
   ra::clear_error();
   return ra::decode_impl(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0, out,
                          lse, (hipStream_t)stream);
+}
+
+int ring_attn_ffn_blockwise(const void* x, const void* w1, const float* b1, const void* w2, const float* b2, int rows,
+                            int hidden, int ffn, int chunk_rows, float* y, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::ffn_impl(x, w1, b1, w2, b2, rows, hidden, ffn, chunk_rows, y, (hipStream_t)stream);
 }
 
 int ring_attn_mfma_rate(int iters, float* sink, double* tflops, ra_stream_t stream) {

@@ -28,10 +28,12 @@ from .dense import (attention_fwd, attention_bwd, brute_force_fwd, positions_for
 from .ring import (ring_steps, simulate_ring, ring_forward, online_block_forward,
                    merge_partials, merge_partials_scalar, zigzag_positions, visible_pairs_per_rank)
 from .decode import decode_forward, decode_by_partials
+from .ffn import ffn_blockwise, ffn_forward, gelu
 
 __all__ = [
     "attention_fwd", "attention_bwd", "brute_force_fwd", "positions_for_block",
     "sampled_rows_fwd", "ring_steps", "simulate_ring", "ring_forward",
     "online_block_forward", "merge_partials", "merge_partials_scalar",
     "decode_forward", "decode_by_partials", "zigzag_positions", "visible_pairs_per_rank",
+    "ffn_forward", "ffn_blockwise", "gelu",
 ]

@@ -182,3 +182,14 @@ def test_zigzag_rejects_odd_block_len_before_any_hip_call():
     vb = (ctypes.c_void_p * 2)(BASE + 0x50000000, BASE + 0x60000000)
     rc = L.ring_attn_fwd_zigzag(BASE, kb, vb, 2, 33, 2, 2, 128, 1, 0, BASE + 0x10000000, BASE + 0x20000000, None)
     assert rc == ra.RA_ERR_INVALID_ARG and b"even" in L.ring_attn_last_error()
+
+
+def test_ffn_validation_before_any_hip_call():
+    L = ra.lib()
+    x, w1, w2, y = BASE, BASE + 0x10000000, BASE + 0x20000000, BASE + 0x30000000
+    assert L.ring_attn_ffn_blockwise(None, w1, None, w2, None, 8, 128, 256, 0, y, None) == ra.RA_ERR_INVALID_ARG
+    assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 0, 128, 256, 0, y, None) == ra.RA_ERR_INVALID_ARG
+    assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 96, 256, 0, y, None) == ra.RA_ERR_UNSUPPORTED
+    assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 200, 0, y, None) == ra.RA_ERR_UNSUPPORTED
+    assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 256, -1, y, None) == ra.RA_ERR_INVALID_ARG
+    assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 256, 0, x + 64, None) == ra.RA_ERR_INVALID_ARG

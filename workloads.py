@@ -104,6 +104,44 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    """Blockwise feedforward on one rank's block: y = GELU(x W1^T + b1) W2^T + b2."""
+
+    name: str
+    rows: int        # tokens of the block
+    hidden: int      # h (= heads x head_dim of the attention it follows)
+    ffn: int         # intermediate width (4h)
+    chunk_rows: int  # rows per feedforward block
+    seed: int
+    description: str = ""
+
+    def flop(self) -> float:
+        """Two GEMMs of 2 * rows * hidden * ffn flop each."""
+        return 4.0 * self.rows * self.hidden * self.ffn
+
+
+FFN_WORKLOADS: Dict[str, FfnWorkload] = {
+    w.name: w
+    for w in [
+        FfnWorkload("ffn_block8192_h4096_f16384", 8192, 4096, 16384, 2048, 7,
+                    "one rank's 8192-token block of the causal 128k workload (h = 32 x 128), 4h intermediate, "
+                    "blocks of 2048 rows"),
+    ]
+}
+
+
+def gen_ffn(w: FfnWorkload):
+    """Seeded ffn inputs: x ~ N(0,1), W1 ~ N(0, 1/hidden), W2 ~ N(0, 1/ffn) (bf16-rounded),
+    b1, b2 ~ N(0, 0.1^2) in fp32 -- unit-scale activations at every layer."""
+    x = gen_small(w.seed, (w.rows, w.hidden), "bf16", 1.0, 0)
+    w1 = gen_small(w.seed, (w.ffn, w.hidden), "bf16", 1.0 / np.sqrt(w.hidden), 1)
+    w2 = gen_small(w.seed, (w.hidden, w.ffn), "bf16", 1.0 / np.sqrt(w.ffn), 2)
+    b1 = gen_small(w.seed, (w.ffn,), "f32", 0.1, 3)
+    b2 = gen_small(w.seed, (w.hidden,), "f32", 0.1, 4)
+    return x, w1, b1, w2, b2
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
