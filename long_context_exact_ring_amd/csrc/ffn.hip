@@ -11,9 +11,11 @@
 // H = GELU(X W1^T + b1) of that chunk only, a second GEMM reads it back.
 //
 // GEMM kernel (gemm_bt_kernel): C[m][n] = sum_k A[m][k] B[n][k] with both
-// operands k-contiguous.  A 128x128 workgroup tile, four waves of 64x64, a
-// k-step of 64 staged global -> LDS by LDS DMA into swizzled 128-byte rows
-// (double-buffered, one barrier per k-step).  The MFMA computes the tile
+// operands k-contiguous.  A 256x256 workgroup tile of eight 64x128 waves
+// (0.75 KB of LDS reads per MFMA) where the shape fills the chip with it,
+// else 128x128 with four 64x64 waves; a k-step of 64 staged global -> LDS by
+// LDS DMA into swizzled 128-byte rows (double-buffered, one barrier per
+// k-step).  The MFMA computes the tile
 // transposed (weights as the A operand, activation rows as B), so a lane ends
 // up holding four consecutive output columns of one row: bias, GELU and the
 // bf16 / fp32 stores work on contiguous 8- or 16-byte pieces.
@@ -31,34 +33,43 @@ __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.f + er
 
 }  // namespace
 
-template <bool GELU_BF16_OUT>
-__global__ __launch_bounds__(256) void gemm_bt_kernel(GemmArgs a) {
+// A wave computes TM x TN transposed 32x32 tiles (TM along the activation
+// rows, TN along the weight rows); the workgroup is WGM x WGN waves.
+template <int TM, int TN, int WGM, int WGN, bool GELU_BF16_OUT>
+__global__ __launch_bounds__(WGM * WGN * 64) void gemm_bt_kernel(GemmArgs a) {
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
   constexpr int ROWB = kGemmBK * 2;              // 128 bytes per tile row
-  constexpr int TILEB = kGemmBM * ROWB;          // 16 KB per operand tile
-  constexpr int STAGE = 2 * TILEB;               // activation tile, weight tile
+  constexpr int ATILE = BM * ROWB, BTILE = BN * ROWB;
+  constexpr int STAGE = ATILE + BTILE;           // activation tile, weight tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 31, hf = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wu & 1, wn = wu >> 1;  // this wave's 64x64 quadrant
+  const int wm = wu % WGM, wn = wu / WGM;  // this wave's (TM*32) x (TN*32) piece
 
   // workgroup -> (row tile, column tile); consecutive workgroups share the
   // activation rows (column tiles vary fastest within an XCD's share)
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ntn = a.n / kGemmBN;
+  const int ntn = a.n / BN;
   const int tn = logical % ntn, tm = logical / ntn;
-  const int m0 = tm * kGemmBM, n0 = tn * kGemmBN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   // DMA lane offsets: a 1 KB instruction moves 8 rows of 128 bytes
   constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16;  // 8 rows, 8 chunks per row
-  constexpr int NI = kGemmBM / RPI;                  // 16 instructions per operand tile
-  constexpr int IPW = NI / 4;                        // 4 per wave
-  uint32_t aoff[IPW], boff[IPW];
+  constexpr int NIA = BM / RPI, NIB = BN / RPI;      // instructions per operand tile
+  static_assert(NIA % NW == 0 && NIB % NW == 0, "tile DMA must split evenly over the waves");
+  constexpr int IPA = NIA / NW, IPB = NIB / NW;
+  uint32_t aoff[IPA], boff[IPB];
 #pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int r = (wu * IPW + j) * RPI + lane / CPR, slot = lane % CPR;
+  for (int j = 0; j < IPA; ++j) {
+    const int r = (wu * IPA + j) * RPI + lane / CPR, slot = lane % CPR;
     const int mr = min(m0 + r, a.m - 1);  // rows past the end re-read the last row (never stored)
     aoff[j] = (uint32_t)(((size_t)mr * a.lda + (slot ^ swz<64>(r)) * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < IPB; ++j) {
+    const int r = (wu * IPB + j) * RPI + lane / CPR, slot = lane % CPR;
     boff[j] = (uint32_t)(((size_t)(n0 + r) * a.ldb + (slot ^ swz<64>(r)) * 8) * 2);
   }
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.a);
@@ -66,18 +77,20 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(GemmArgs a) {
   auto issue = [&](int ks, unsigned char* st) {
     const size_t kb = (size_t)ks * kGemmBK * 2;
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const uint32_t q = (uint32_t)(wu * IPW + j) * 1024;
-      lds_dma16_off(abase + kb, aoff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + q)));
-      lds_dma16_off(bbase + kb, boff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + TILEB + q)));
-    }
+    for (int j = 0; j < IPA; ++j)
+      lds_dma16_off(abase + kb, aoff[j],
+                    __builtin_amdgcn_readfirstlane(lds_addr(st + (uint32_t)(wu * IPA + j) * 1024)));
+#pragma unroll
+    for (int j = 0; j < IPB; ++j)
+      lds_dma16_off(bbase + kb, boff[j],
+                    __builtin_amdgcn_readfirstlane(lds_addr(st + ATILE + (uint32_t)(wu * IPB + j) * 1024)));
   };
 
-  f32x16_t acc[2][2];  // [weight-row tile][activation-row tile], transposed 32x32 tiles
+  f32x16_t acc[TN][TM];  // [weight-row tile][activation-row tile], transposed 32x32 tiles
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
 
   const int nk = a.k / kGemmBK;
   issue(0, smem);
@@ -86,33 +99,32 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(GemmArgs a) {
     __syncthreads();                                     // ... everyone's; the other stage is free
     if (ks + 1 < nk) issue(ks + 1, smem + ((ks + 1) & 1) * STAGE);
     const unsigned char* at = smem + (ks & 1) * STAGE;  // activation rows
-    const unsigned char* bt = at + TILEB;               // weight rows
+    const unsigned char* bt = at + ATILE;               // weight rows
 #pragma unroll
     for (int kk = 0; kk < kGemmBK / 16; ++kk) {
-      Frag<bf16_storage> wf[2], xf[2];
+      Frag<bf16_storage> wf[TN], xf[TM];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        wf[i] = row_frag<64>(bt, wn * 64 + i * 32 + n, kk, hf);
-        xf[i] = row_frag<64>(at, wm * 64 + i * 32 + n, kk, hf);
-      }
+      for (int i = 0; i < TN; ++i) wf[i] = row_frag<64>(bt, (wn * TN + i) * 32 + n, kk, hf);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < TM; ++j) xf[j] = row_frag<64>(at, (wm * TM + j) * 32 + n, kk, hf);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma(acc[i][j], wf[i], xf[j]);
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) mma(acc[i][j], wf[i], xf[j]);
     }
   }
 
-  // epilogue: lane holds output row m = m0 + wm*64 + j*32 + n and columns
-  // n0 + wn*64 + i*32 + crow(r, hf) for the 16 accumulator registers r
+  // epilogue: lane holds output row m = m0 + (wm*TM + j)*32 + n and columns
+  // n0 + (wn*TN + i)*32 + crow(r, hf) for the 16 accumulator registers r
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + wm * 64 + j * 32 + n;
+  for (int j = 0; j < TM; ++j) {
+    const int m = m0 + (wm * TM + j) * 32 + n;
     if (m >= a.m) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = n0 + wn * 64 + i * 32 + q4 * 8 + hf * 4;  // four consecutive columns
+        const int c0 = n0 + (wn * TN + i) * 32 + q4 * 8 + hf * 4;  // four consecutive columns
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -134,15 +146,32 @@ __global__ __launch_bounds__(256) void gemm_bt_kernel(GemmArgs a) {
   }
 }
 
+#ifndef RA_GEMM_BIG
+#define RA_GEMM_BIG 1  // 0: always the 128x128 tile; 1: 256-wide tiles where the shape allows
+#endif
+
+template <int TM, int TN, int WGM, int WGN>
+static hipError_t launch_gemm_cfg(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st) {
+  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
+  const long nblk = (long)((a.m + BM - 1) / BM) * (a.n / BN);
+  if (gelu_bf16_out)
+    hipLaunchKernelGGL((gemm_bt_kernel<TM, TN, WGM, WGN, true>), dim3((unsigned)nblk), dim3(WGM * WGN * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_bt_kernel<TM, TN, WGM, WGN, false>), dim3((unsigned)nblk), dim3(WGM * WGN * 64), 0, st,
+                       a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bt(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st) {
   if (a.m < 1 || a.n % kGemmBN != 0 || a.k % kGemmBK != 0 || a.n < kGemmBN || a.k < kGemmBK)
     return hipErrorInvalidValue;
-  const long nblk = (long)((a.m + kGemmBM - 1) / kGemmBM) * (a.n / kGemmBN);
-  if (gelu_bf16_out)
-    hipLaunchKernelGGL(gemm_bt_kernel<true>, dim3((unsigned)nblk), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(gemm_bt_kernel<false>, dim3((unsigned)nblk), dim3(256), 0, st, a);
-  return hipGetLastError();
+  // 256x256 tiles (8 waves of 64x128) when the columns allow it and the grid still fills the chip
+  if (RA_GEMM_BIG && a.n % 256 == 0 && (long)((a.m + 255) / 256) * (a.n / 256) >= 256)
+    return launch_gemm_cfg<2, 4, 4, 2>(a, gelu_bf16_out, st);
+  // 128x256 tiles (four 64x128 waves) for shorter row blocks
+  if (RA_GEMM_BIG >= 2 && a.n % 256 == 0 && (long)((a.m + 127) / 128) * (a.n / 256) >= 256)
+    return launch_gemm_cfg<2, 4, 2, 2>(a, gelu_bf16_out, st);
+  return launch_gemm_cfg<2, 2, 2, 2>(a, gelu_bf16_out, st);
 }
 
 int gemm_tile_n() { return kGemmBN; }
