@@ -316,16 +316,38 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
 
   const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
   const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
+  // whole tiles: a uniform base plus fixed per-lane offsets; the ragged last
+  // tile re-reads its last row for the rows past the end (masked)
+  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16, NI = BC / RPI;
+  constexpr int IPW = (NI + NW - 1) / NW;
+  uint32_t goff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wu * IPW + j) * RPI + lane / CPR, slot = lane % CPR;
+    goff[j] = (uint32_t)(r * kvstride + (slot ^ swz<D>(r)) * 8) * 2;
+  }
   auto issue = [&](int t, unsigned char* st) {
-    dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
-    dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
+    if ((t + 1) * BC <= a.len) {
+      const size_t tb = (size_t)t * BC * kvstride * 2;
+      const unsigned char* kb = reinterpret_cast<const unsigned char*>(kbase) + tb;
+      const unsigned char* vb = reinterpret_cast<const unsigned char*>(vbase) + tb;
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int q = wu * IPW + j;
+        if (NI % NW != 0 && q >= NI) break;  // uniform
+        lds_dma16_off(kb, goff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + q * 1024)));
+        lds_dma16_off(vb, goff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + TILEB + q * 1024)));
+      }
+    } else {
+      dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
+      dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
+    }
   };
+  const LdsOperandOffsets<D> lo(lane, 0);  // row reads of K and V, transposed reads of K
 
   auto tile = [&](int t, const unsigned char* st, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int t0 = t * BC;
-    const unsigned char* kn = st;
-    const unsigned char* vn = st + TILEB;
     if (MASKED && a.diag && t0 > row0 + 31) return;  // wholly in this wave's future
     f32x16_t s[BC / 32], dp[BC / 32];
 #pragma unroll
@@ -334,8 +356,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
       dp[kt] = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        mma(s[kt], row_frag<D>(kn, kt * 32 + n, ks, hf), qf[ks]);
-        mma(dp[kt], row_frag<D>(vn, kt * 32 + n, ks, hf), of[ks]);
+        const Frag<bf16_storage> kf{*reinterpret_cast<const uint4*>(st + kt * 32 * ROWB + lo.k[ks])};
+        const Frag<bf16_storage> vf{*reinterpret_cast<const uint4*>(st + TILEB + kt * 32 * ROWB + lo.k[ks])};
+        mma(s[kt], kf, qf[ks]);
+        mma(dp[kt], vf, of[ks]);
       }
     }
     const int lim = (a.diag ? min(qi, a.len - 1) : a.len - 1) - t0;  // visible local keys: <= lim
@@ -356,21 +380,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) ds8[e] = dp[kc >> 1][(kc & 1) * 8 + e];
       const Frag<bf16_storage> sf = frag_from_f32<bf16_storage>(ds8);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) mma(dqT[dt], tr_frag<D>(kn, dt * 32, kc, lane), sf);
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint2 v0 = ds_read_tr16(st + kc * 16 * ROWB + lo.v[dt][0]);
+        const uint2 v1 = ds_read_tr16(st + kc * 16 * ROWB + lo.v[dt][1]);
+        mma(dqT[dt], Frag<bf16_storage>{make_uint4(v0.x, v0.y, v1.x, v1.y)}, sf);
+      }
     }
   };
 
-  auto step = [&](int t, auto masked_tag) {
+  // ST: the stage of tile t when known at compile time (immediate LDS offsets), else -1
+  auto step = [&](int t, auto masked_tag, auto stage_tag) {
+    constexpr int ST = decltype(stage_tag)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * STAGE);
-    tile(t, smem + (t & 1) * STAGE, masked_tag);
+    const int sc = ST >= 0 ? ST : (t & 1);
+    if (t + 1 < ntiles) issue(t + 1, smem + (1 - sc) * STAGE);
+    tile(t, smem + sc * STAGE, masked_tag);
   };
 
   issue(0, smem);
   int t = 0;
-  for (; t < nfull; ++t) step(t, std::false_type{});
-  for (; t < ntiles; ++t) step(t, std::true_type{});
+  for (; t + 1 < nfull; t += 2) {
+    step(t, std::false_type{}, std::integral_constant<int, 0>{});
+    step(t + 1, std::false_type{}, std::integral_constant<int, 1>{});
+  }
+  for (; t < nfull; ++t) step(t, std::false_type{}, std::integral_constant<int, -1>{});
+  for (; t < ntiles; ++t) step(t, std::true_type{}, std::integral_constant<int, -1>{});
 
   if (qi >= a.len) return;
   float* dqp = a.dq + (size_t)qi * qstride + (size_t)head * D;

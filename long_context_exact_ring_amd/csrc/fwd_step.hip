@@ -226,34 +226,9 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
 // ============================================================================
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
-// Per-lane byte offsets of the operand reads within one LDS stage (a K tile
-// then a V tile).  A swizzled row's chunk order repeats every 16 rows, so the
-// reads of other 32-key (K) or 16-key (V) slices differ from these by
-// immediates, and with the stage known at compile time every read is one
-// ds_read with no address arithmetic.
-template <int D>
-struct FwdLdsOffsets {
-  uint32_t k[D / 16];     // row_frag(n, ks, hf) of the K tile
-  uint32_t v[D / 32][2];  // the two transposed reads of tr_frag(dt * 32, kc = 0) of the V tile
-  __device__ __forceinline__ FwdLdsOffsets(int lane, int tileb) {
-    const int n = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) k[ks] = n * (D * 2) + (((ks * 2 + hf) ^ swz<D>(n)) * 16);
-    const int gq = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int dcol = dt * 32 + (gq & 1) * 16 + 4 * (i16 & 3);
-        const int r = u * 8 + (gq >> 1) * 4 + (i16 >> 2);
-        v[dt][u] = tileb + r * (D * 2) + (((dcol >> 3) ^ swz<D>(r)) * 16) + (dcol & 7) * 2;
-      }
-  }
-};
-
 template <int D, int BC, int NW, int RG, bool MASKED>
 __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned char* stage_lds,
-                                              const FwdLdsOffsets<D>& lo,
+                                              const LdsOperandOffsets<D>& lo,
                                               const Frag<bf16_storage> (&qf)[RG][D / 16],
                                               f32x16_t (&o)[RG][D / 32], float (&m_run)[RG], float (&l_run)[RG],
                                               int t0, int qi0, int n, int hf, int lane) {
@@ -429,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
   // (diagonal band, ragged tail) take the masked instantiation
   const int wg_first_row = rt * R;
   const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
-  const FwdLdsOffsets<D> lo(lane, TILEB);
+  const LdsOperandOffsets<D> lo(lane, TILEB);
   // one unmasked tile; ST is its stage when known at compile time (then every
   // LDS read address is an offset register plus an immediate), else -1
   auto open_step = [&](int t, auto stage_tag) {

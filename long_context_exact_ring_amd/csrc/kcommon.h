@@ -206,6 +206,33 @@ __device__ __forceinline__ Frag<bf16_storage> row_frag(const unsigned char* tile
   return Frag<bf16_storage>{*reinterpret_cast<const uint4*>(tile + r * (D * 2) + c * 16)};
 }
 
+// Per-lane byte offsets of the operand reads of a stage holding swizzled
+// [rows][D] bf16 tiles: `k` for row_frag(n, ks, hf) reads of a tile at the
+// stage start, `v` for the transposed tr_frag(dt * 32, kc = 0) reads of a
+// tile `tileb` bytes in.  A swizzled row's chunk order repeats every 16 rows,
+// so reads of other 32-row (row_frag) or 16-row (tr_frag) slices differ from
+// these by immediates, and with the stage known at compile time every read is
+// one ds_read with no address arithmetic.
+template <int D>
+struct LdsOperandOffsets {
+  uint32_t k[D / 16];     // row_frag(n, ks, hf) of the tile at the stage start
+  uint32_t v[D / 32][2];  // the two transposed reads of tr_frag(dt * 32, kc = 0) of the tile at tileb
+  __device__ __forceinline__ LdsOperandOffsets(int lane, int tileb) {
+    const int n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k[ks] = n * (D * 2) + (((ks * 2 + hf) ^ swz<D>(n)) * 16);
+    const int gq = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int dcol = dt * 32 + (gq & 1) * 16 + 4 * (i16 & 3);
+        const int r = u * 8 + (gq >> 1) * 4 + (i16 >> 2);
+        v[dt][u] = tileb + r * (D * 2) + (((dcol >> 3) ^ swz<D>(r)) * 16) + (dcol & 7) * 2;
+      }
+  }
+};
+
 // LDS DMA of rows [t0, t0 + ROWS) of a token-major [len][heads][D] bf16 tensor
 // (head offset already applied, `stride` elements between rows) into a
 // swizzled [ROWS][D] tile.  The NW waves of the workgroup split the 1 KB
