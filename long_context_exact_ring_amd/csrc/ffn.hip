@@ -48,11 +48,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bt_kernel(GemmArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wu % WGM, wn = wu / WGM;  // this wave's (TM*32) x (TN*32) piece
 
-  // workgroup -> (row tile, column tile); consecutive workgroups share the
-  // activation rows (column tiles vary fastest within an XCD's share)
+  // workgroup -> (row tile, column tile).  Consecutive workgroups (one XCD's
+  // share, one L2) share a weight tile when the weights outweigh the
+  // activation rows and the contraction is short (measured: the up-projection,
+  // k = hidden); otherwise they share the activation rows (the down-projection).
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ntn = a.n / BN;
-  const int tn = logical % ntn, tm = logical / ntn;
+  const int ntn = a.n / BN, ntm = (a.m + BM - 1) / BM;
+  const bool weights_larger = a.n > a.m && a.k <= 8192;
+  const int tn = weights_larger ? logical / ntm : logical % ntn;
+  const int tm = weights_larger ? logical % ntm : logical / ntn;
   const int m0 = tm * BM, n0 = tn * BN;
 
   // DMA lane offsets: a 1 KB instruction moves 8 rows of 128 bytes
