@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--workload", default="causal_128k_h32_d128")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the rocm-smi shader-clock sample (for runs under a profiler)")
     p.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU oracle sample")
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a reference kernel of "
@@ -147,8 +149,12 @@ def read_sclk_mhz():
     """Current shader clock of GPU 0 from rocm-smi (None when unavailable); never blocks > 15 s."""
     import re
     import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15)
+    import shutil
+    smi = shutil.which("rocm-smi")
+    if smi is None:
+        return None
+    try:  # rocm-smi is a Python script: run it with this interpreter, not through its #! line
+        r = subprocess.run([sys.executable, smi, "--showclocks"], capture_output=True, text=True, timeout=15)
     except Exception:
         return None
     for line in r.stdout.splitlines():
@@ -371,17 +377,28 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str):
             continue
         if kind == "ffn_up" and not name.endswith("true>") or kind == "ffn_down" and not name.endswith("false>"):
             continue
-        for fname, sha in t.get("source_sha256", {}).items():
+        recorded = t.get("source_sha256", {})
+        for fname in kernel_sources(name):
             src = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc", fname)
-            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+            if fname not in recorded or hashlib.sha256(open(src, "rb").read()).hexdigest() != recorded[fname]:
                 return None  # the kernel changed since its counters were taken
-        if not t.get("source_sha256"):
-            return None
         return round(t["read_bytes"] + t["write_bytes"])
     return None
 
 
-HASHED_SOURCES = ("fwd_step.hip", "bwd_bf16.hip", "decode.hip", "ffn.hip", "kcommon.h")
+COMMON_SOURCES = ("kcommon.h", "kernels.h")
+KERNEL_SOURCES = (("fwd_bf16_kernel", ("fwd_step.hip", "fwd_common.h", "tile_stage.h")),
+                  ("bwd_dkdv_bf16_kernel", ("bwd_bf16.hip",)), ("bwd_dq_bf16_kernel", ("bwd_bf16.hip",)),
+                  ("bwd_pre_kernel", ("bwd_step.hip", "tile_stage.h")), ("decode_", ("decode.hip",)),
+                  ("gemm_bt_kernel", ("ffn.hip",)), ("merge", ("merge.hip",)))
+
+
+def kernel_sources(name: str):
+    """The source files a kernel's code comes from (its own file plus the shared headers)."""
+    for pattern, files in KERNEL_SOURCES:
+        if pattern in name:
+            return files + COMMON_SOURCES
+    return tuple(sorted({f for _, fs in KERNEL_SOURCES for f in fs})) + COMMON_SOURCES
 REF_COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -428,15 +445,15 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
         print(f"| `{name}` | {n} | {f:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
     # merge into the committed record; every kernel entry carries the source hashes it was taken with
     csrc = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc")
-    hashes = {f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest() for f in HASHED_SOURCES}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     known = rec.get("kernels", {})
     for name, t in kernels.items():
-        known[name] = dict(t, source_sha256=hashes)
+        known[name] = dict(t, source_sha256={f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+                                             for f in kernel_sources(name)})
     rec = {"kernels": known,
            "note": "HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; an entry is "
-                   "stale once any source listed with it has changed"}
+                   "stale once any source file listed with it has changed"}
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     rows = list(csv.DictReader(open(stats_csv)))
@@ -517,14 +534,15 @@ def main():
     torch.cuda.synchronize()
     timing["on"] = True
     clock = ClockSampler(min(2.0, 0.3 * args.steps))
-    clock.start()
+    if not args.no_clock:
+        clock.start()
     evs[0].record()
     for i in range(args.steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
     timing["on"] = False
-    sclk = clock.join()
+    sclk = None if args.no_clock else clock.join()
     ms_total = evs[0].elapsed_time(evs[-1])
     rank_ms = {}
     for r, marks in rank_ev.items():

@@ -109,6 +109,7 @@ struct GemmArgs {
   void* c;            // [m][ldc] bf16 or fp32
   const float* bias;  // [n] or nullptr
   int m, n, k, lda, ldb, ldc;
+  int group = 0;      // row tiles per band of the workgroup order (set by launch_gemm_bt)
 };
 hipError_t launch_gemm_bt(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st);
 int gemm_tile_n();
