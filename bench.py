@@ -39,7 +39,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="causal_128k_h32_d128")
     p.add_argument("--fwd-only", action="store_true", help="time only the forward of every rank")
     p.add_argument("--no-cpu-baseline", action="store_true")
