@@ -438,346 +438,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
 }
 
 
-// ============================================================================
-// bf16 path, "ping-pong" schedule.  The eight waves of a workgroup form two
-// groups of four (one wave of each group per SIMD).  Each wave alternates an
-// MFMA cluster -- PV of tile t-1 followed by S = K Q^T of tile t -- with a VALU
-// cluster -- the online softmax of tile t -- and the second group runs one
-// cluster behind the first.  A workgroup barrier at every cluster boundary
-// keeps the two groups in opposite phases, so one wave per SIMD feeds the
-// matrix core while the other does the exponentials.  K/V tiles rotate
-// through three LDS buffers: tile t+1 is copied (LDS DMA) while tiles t-1 (V,
-// for PV) and t (K, for S) are being read.
-// ============================================================================
-template <int D, int BC>
-__device__ __forceinline__ void pp_softmax(const FwdArgs& a, f32x16_t (&s)[BC / 32], f32x16_t (&o)[D / 32],
-                                           float& m_run, float& l_run, Frag<bf16_storage> (&pf)[BC / 16],
-                                           bool masked, int lim, int hf) {
-  if (__builtin_expect(masked, 0)) {
-#pragma unroll
-    for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (kt * 32 + crow(i, hf) > lim) s[kt][i] = kNegInf;
-  }
-  float mx = kNegInf;
-#pragma unroll
-  for (int kt = 0; kt < BC / 32; ++kt)
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kt][i], s[kt][i + 1]));
-  mx = fmaxf(mx, swap_halves(mx));
-  const float mxs = mx * a.scale_log2;
-  if (__builtin_amdgcn_ballot_w64(mxs > m_run + kRescaleThreshold) != 0) {
-    const float m_new = fmaxf(m_run, mxs);
-    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    m_run = m_new;
-  }
-  const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-  for (int kc = 0; kc < BC / 16; ++kc) {
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = fast_exp2(__builtin_fmaf(s[kc >> 1][(kc & 1) * 8 + e], a.scale_log2, -m_use));
-      l_run += p[e];
-    }
-    pf[kc] = frag_from_f32<bf16_storage>(p);
-  }
-}
-
-template <int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_pp_kernel(FwdArgs a) {
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = BC * ROWB;
-  constexpr int STAGE = 2 * TILEB;
-  constexpr int NBUF = 3;
-  constexpr int RPI = 1024 / ROWB;
-  constexpr int CPR = ROWB / 16;
-  constexpr int IPW = BC / RPI / NW;
-  static_assert(NW % 2 == 0, "two wave groups");
-  static_assert(IPW >= 1 && (BC / RPI) % NW == 0, "tile rows must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wu / (NW / 2);
-
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int R = NW * 32 / a.hpw;
-  const int nrt = (a.len + R - 1) / R;
-  int rt = logical % nrt;
-  const int rest = logical / nrt;
-  const int hs = rest % a.hsub;
-  const int g = rest / a.hsub;
-  if (a.diag) rt = nrt - 1 - rt;
-  const int wpr = NW / a.hpw;
-  const int head = g * a.group + hs * a.hpw + wu / wpr;
-  const int row0 = rt * R + (wu % wpr) * 32;
-  const int qi = row0 + n;
-  const int wg_first_row = rt * R;
-  const int wg_last_row = min(rt * R + R, a.len) - 1;
-  int ntiles = (a.len + BC - 1) / BC;
-  if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
-  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
-  // tiles [0, nact) hold keys at or before this wave's last row
-  const int nact = a.diag ? min(ntiles, (row0 + 31) / BC + 1) : ntiles;
-  const int lim_base = a.diag ? min(qi, a.len - 1) : a.len - 1;
-
-  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
-  const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
-  const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
-
-  Frag<bf16_storage> qf[D / 16];
-  {
-    const bf16_storage* qp =
-        reinterpret_cast<const bf16_storage*>(a.q) + (size_t)min(qi, a.len - 1) * qstride + (size_t)head * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = frag_load<bf16_storage>(qp + ks * 16);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  const int lrow = lane / CPR, slot = lane % CPR;
-  uint32_t koff[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int r = (wu * IPW + j) * RPI + lrow;
-    koff[j] = (uint32_t)(r * kvstride + (slot ^ swz<D>(r)) * 8) * 2;
-  }
-  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
-  const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
-  auto buf = [&](int t) { return smem + (t % NBUF) * STAGE; };
-  auto issue = [&](int t) {
-    unsigned char* kd = buf(t);
-    unsigned char* vd = kd + TILEB;
-    const int t0 = t * BC;
-    const size_t tb = (size_t)t0 * kvstride * 2;
-    if (t0 + BC <= a.len) {
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        const int q = wu * IPW + j;
-        lds_dma16_off(kbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
-        lds_dma16_off(vbytes + tb, koff[j], __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        const int q = wu * IPW + j;
-        const int r = q * RPI + lrow;
-        const int row = min(t0 + r, a.len - 1);
-        const bf16_storage* ks = kbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
-        const bf16_storage* vs = vbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
-        lds_dma16(ks, __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
-        lds_dma16(vs, __builtin_amdgcn_readfirstlane(lds_addr(vd + q * 1024)));
-      }
-    }
-  };
-
-  float m_run = kNegInf, l_run = 0.f;
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  f32x16_t s[BC / 32];
-  Frag<bf16_storage> pf[BC / 16];
-
-  // slot boundary sl: every wave waits for its share of the DMA issued two
-  // slots ago (tile sl/2), joins the barrier, and on even slots starts the
-  // DMA of tile sl/2 + 1 into the buffer freed by tile sl/2 - 2.
-  auto slot_begin = [&](int sl) {
-    if ((sl & 1) == 0 && sl >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if ((sl & 1) == 0 && sl / 2 + 1 < ntiles) issue(sl / 2 + 1);
-  };
-  auto mfma_cluster = [&](int t) {  // PV of tile t-1, then S of tile t
-    if (t >= 1 && t - 1 < nact) {
-      const unsigned char* vt = buf(t - 1) + TILEB;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int kc = 0; kc < BC / 16; ++kc) mma(o[dt], tr_frag<D>(vt, dt * 32, kc, lane), pf[kc]);
-    }
-    if (t < nact) {
-      const unsigned char* kt = buf(t);
-#pragma unroll
-      for (int k2 = 0; k2 < BC / 32; ++k2) {
-        s[k2] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) mma(s[k2], row_frag<D>(kt, k2 * 32 + n, ks, hf), qf[ks]);
-      }
-    }
-  };
-  auto valu_cluster = [&](int t) {
-    if (t < nact) pp_softmax<D, BC>(a, s, o, m_run, l_run, pf, t >= nfull, lim_base - t * BC, hf);
-  };
-
-  issue(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (grp == 0) {  // MFMA cluster on even slots
-    for (int t = 0; t < ntiles; ++t) {
-      slot_begin(2 * t);
-      mfma_cluster(t);
-      slot_begin(2 * t + 1);
-      valu_cluster(t);
-    }
-    slot_begin(2 * ntiles);
-    mfma_cluster(ntiles);
-    slot_begin(2 * ntiles + 1);
-  } else {  // one cluster behind: MFMA cluster on odd slots
-    slot_begin(0);
-    for (int t = 0; t < ntiles; ++t) {
-      slot_begin(2 * t + 1);
-      mfma_cluster(t);
-      slot_begin(2 * t + 2);
-      valu_cluster(t);
-    }
-    slot_begin(2 * ntiles + 1);
-    mfma_cluster(ntiles);
-  }
-  fwd_epilogue<D>(a, o, m_run, l_run, head, qi, hf);
-}
-
-
-// ============================================================================
-// bf16 path, software-pipelined (FA3-style within a wave): in iteration t the
-// wave issues the S MFMAs of tile t+1 interleaved with the softmax VALU work
-// of tile t (scheduling groups force the interleave, since a wave issues in
-// order and would otherwise stall its VALU stream behind back-to-back MFMAs),
-// then the PV MFMAs of tile t.  K/V tiles rotate through three LDS buffers,
-// the DMA running two tiles ahead.
-// ============================================================================
-template <int D, int BC>
-__device__ __forceinline__ void sp_scores(const unsigned char* kt_lds, const Frag<bf16_storage> (&qf)[D / 16],
-                                          f32x16_t (&s)[BC / 32], int n, int hf) {
-#pragma unroll
-  for (int kt = 0; kt < BC / 32; ++kt) {
-    s[kt] = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) mma(s[kt], row_frag<D>(kt_lds, kt * 32 + n, ks, hf), qf[ks]);
-  }
-}
-
-template <int D, int BC>
-__device__ __forceinline__ void sp_pv(const unsigned char* vt_lds, const Frag<bf16_storage> (&pf)[BC / 16],
-                                      f32x16_t (&o)[D / 32], int lane) {
-#pragma unroll
-  for (int kc = 0; kc < BC / 16; ++kc)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) mma(o[dt], tr_frag<D>(vt_lds, dt * 32, kc, lane), pf[kc]);
-}
-
-template <int D, int BC, int NW, bool INTERLEAVE>
-__global__ __launch_bounds__(NW * 64) void fwd_sp_kernel(FwdArgs a) {
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = BC * ROWB;
-  constexpr int STAGE = 2 * TILEB;
-  constexpr int NBUF = 3;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int R = NW * 32 / a.hpw;
-  const int nrt = (a.len + R - 1) / R;
-  int rt = logical % nrt;
-  const int rest = logical / nrt;
-  const int hs = rest % a.hsub;
-  const int g = rest / a.hsub;
-  if (a.diag) rt = nrt - 1 - rt;
-  const int wpr = NW / a.hpw;
-  const int head = g * a.group + hs * a.hpw + wu / wpr;
-  const int row0 = rt * R + (wu % wpr) * 32;
-  const int qi = row0 + n;
-  const int wg_first_row = rt * R;
-  const int wg_last_row = min(rt * R + R, a.len) - 1;
-  int ntiles = (a.len + BC - 1) / BC;
-  if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
-  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
-  const int nact = a.diag ? min(ntiles, (row0 + 31) / BC + 1) : ntiles;  // tiles with keys <= this wave's rows
-  const int lim_base = a.diag ? min(qi, a.len - 1) : a.len - 1;
-
-  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
-  const bf16_storage* kbase = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D;
-  const bf16_storage* vbase = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)g * D;
-
-  Frag<bf16_storage> qf[D / 16];
-  {
-    const bf16_storage* qp =
-        reinterpret_cast<const bf16_storage*>(a.q) + (size_t)min(qi, a.len - 1) * qstride + (size_t)head * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = frag_load<bf16_storage>(qp + ks * 16);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  auto buf = [&](int t) { return smem + (t % NBUF) * STAGE; };
-  auto issue = [&](int t) {
-    dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.len, buf(t), wu, lane);
-    dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.len, buf(t) + TILEB, wu, lane);
-  };
-
-  float m_run = kNegInf, l_run = 0.f;
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16_t{};
-  f32x16_t s_cur[BC / 32], s_nxt[BC / 32];
-  Frag<bf16_storage> pf[BC / 16];
-
-  issue(0);
-  if (ntiles > 1) issue(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (nact > 0) sp_scores<D, BC>(buf(0), qf, s_cur, n, hf);
-
-  auto top = [&](int t) {  // tile t+1 landed everywhere; buffer of tile t-1 free: start tile t+2
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < ntiles) issue(t + 2);
-  };
-  auto copy_scores = [&]() {
-#pragma unroll
-    for (int kt = 0; kt < BC / 32; ++kt) s_cur[kt] = s_nxt[kt];
-  };
-
-  // steady state: tiles t and t+1 both unmasked and active -- one straight-line block
-  int t = 0;
-  const int nsteady = min(nfull, nact) - 1;
-  for (; t < nsteady; ++t) {
-    top(t);
-    sp_scores<D, BC>(buf(t + 1), qf, s_nxt, n, hf);
-    pp_softmax<D, BC>(a, s_cur, o, m_run, l_run, pf, false, 0, hf);
-    if constexpr (INTERLEAVE) {
-      // interleave the next tile's S MFMAs with this tile's softmax VALU
-#pragma unroll
-      for (int i = 0; i < (BC / 32) * (D / 16); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // 6 VALU
-      }
-    }
-    sp_pv<D, BC>(buf(t) + TILEB, pf, o, lane);
-    copy_scores();
-  }
-  // remainder: masked band / ragged tail / last tile
-  for (; t < ntiles; ++t) {
-    top(t);
-    if (t + 1 < nact) sp_scores<D, BC>(buf(t + 1), qf, s_nxt, n, hf);
-    if (t < nact) {
-      pp_softmax<D, BC>(a, s_cur, o, m_run, l_run, pf, t >= nfull, lim_base - t * BC, hf);
-      sp_pv<D, BC>(buf(t) + TILEB, pf, o, lane);
-    }
-    copy_scores();
-  }
-  fwd_epilogue<D>(a, o, m_run, l_run, head, qi, hf);
-}
-
 template <typename T, int D, int BC, int NW>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if (a.hpw < 1 || a.hsub < 1 || NW % a.hpw != 0) return hipErrorInvalidValue;
@@ -793,39 +453,21 @@ constexpr int kFwdWaves = RA_FWD_WAVES;
 // Both paths must share the wave count: the host derives the head packing from it.
 constexpr int kF32Waves = kFwdWaves;
 
-#ifndef RA_FWD_PP
-#define RA_FWD_PP 0
-#endif
-#ifndef RA_FWD_PIPE
-#define RA_FWD_PIPE 0
-#endif
 #ifndef RA_FWD_RG
-#define RA_FWD_RG 1
-#endif
-#ifndef RA_FWD_SP
-#define RA_FWD_SP 0
-#endif
-#ifndef RA_FWD_IL
-#define RA_FWD_IL 1
+#define RA_FWD_RG 1  // 32-row query groups per wave (2: 64 rows at one wave per SIMD)
 #endif
 
 template <int D, int BC, int NW>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   if (a.hpw < 1 || a.hsub < 1 || NW % a.hpw != 0) return hipErrorInvalidValue;
-  const int R = NW * 32 * ((RA_FWD_PP || RA_FWD_SP) ? 1 : RA_FWD_RG) / a.hpw;
+  const int R = NW * 32 * RA_FWD_RG / a.hpw;
   const int nblk = ((a.len + R - 1) / R) * a.hsub * a.hkv;
   if (nblk == 0) return hipSuccess;
-  if constexpr (RA_FWD_SP != 0)
-    hipLaunchKernelGGL((fwd_sp_kernel<D, BC, NW, RA_FWD_IL != 0>), dim3(nblk), dim3(NW * 64), 0, st, a);
-  else if constexpr (RA_FWD_PP != 0)
-    hipLaunchKernelGGL((fwd_pp_kernel<D, BC, NW>), dim3(nblk), dim3(NW * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RA_FWD_RG>), dim3(nblk), dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RA_FWD_RG>), dim3(nblk), dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
-  if (elem_bytes == 2 && RA_FWD_PIPE != 0) return launch_fwd_pipe_bf16(a, head_dim, st);
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_fwd_bf16<64, RA_FWD_BC, kFwdWaves>(a, st);
     if (head_dim == 128) return launch_fwd_bf16<128, RA_FWD_BC, kFwdWaves>(a, st);
@@ -836,8 +478,6 @@ hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipSt
   return hipErrorInvalidValue;
 }
 
-int fwd_waves_per_block(int elem_bytes) {
-  return (elem_bytes == 2 && RA_FWD_PIPE != 0) ? fwd_pipe_waves_per_block() : kFwdWaves;
-}
+int fwd_waves_per_block(int) { return kFwdWaves; }
 
 }  // namespace ra

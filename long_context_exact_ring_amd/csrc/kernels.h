@@ -26,9 +26,6 @@ struct FwdArgs {
 hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 // waves per forward workgroup for an element size (the host packs heads by it)
 int fwd_waves_per_block(int elem_bytes);
-// bf16 forward with two 32-row groups per wave, software-pipelined (fwd_pipe.hip)
-hipError_t launch_fwd_pipe_bf16(const FwdArgs& a, int head_dim, hipStream_t st);
-int fwd_pipe_waves_per_block();
 
 // Backward: Delta = rowsum(dout * out) per (head, row).
 struct BwdPreArgs {
