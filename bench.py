@@ -51,8 +51,8 @@ def parse():
                         "known traffic for scaling profiler byte counters)")
     p.add_argument("--summarize-profiles", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
                    help="no GPU work: turn rocprofv3 CSV output (kernel stats, FETCH_SIZE pass, WRITE_SIZE "
-                        "pass, all taken with --copy-ref-mib) into profiles/traffic.json and print the "
-                        "summary tables")
+                        "pass, all taken with --copy-ref-mib on the workload named by --workload) into "
+                        "profiles/traffic.json and print the summary tables")
     return p.parse_args()
 
 
@@ -251,7 +251,7 @@ def run_decode(args, w, torch, ra):
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9 if dom_ms else None
     roofline = {"bound": "hbm", "kernel": "decode_partial", "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": (achieved / PEAK_HBM_GBS) if achieved else None,
-                "traffic": profiled_traffic("decode_partial", w.head_dim, w.dtype),
+                "traffic": profiled_traffic("decode_partial", w.head_dim, w.dtype, w.name),
                 "algorithmic_bytes": alg_bytes}
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -320,7 +320,7 @@ def run_ffn(args, w, torch, ra):
     achieved = kern.get(dom, {}).get("achieved_tflops")
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": (achieved / PEAK_BF16_TFLOPS) if achieved else None,
-                "traffic": profiled_traffic(dom, 0, "bf16")}
+                "traffic": profiled_traffic(dom, 0, "bf16", w.name)}
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -354,23 +354,26 @@ def run_ffn(args, w, torch, ra):
     print(json.dumps(result), flush=True)
 
 
-def profiled_traffic(kind: str, head_dim: int, dtype: str):
+def profiled_traffic(kind: str, head_dim: int, dtype: str, workload: str):
     """HBM bytes per dispatch of a kernel from the committed profiler summary, or None.
 
-    profiles/traffic.json holds FETCH_SIZE/WRITE_SIZE-derived bytes (scaled by a
-    reference copy) per kernel, each with hashes of the kernel sources it was
-    taken with; any source change since then makes that figure stale (None).
+    profiles/traffic.json holds, per workload, FETCH_SIZE/WRITE_SIZE-derived bytes
+    (scaled by a reference copy) per kernel, each with hashes of the kernel sources
+    it was taken with; a workload that was not profiled, or any source change
+    since, gives None.
     """
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if dtype != "bf16" or not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
+        rec = json.load(f).get("workloads", {}).get(workload)
+    if rec is None:
+        return None
     pattern = {"fwd_step": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_bf16_kernel", "bwd_dq": "bwd_dq_bf16_kernel",
                "decode_partial": "decode_partial_kernel", "ffn_up": "gemm_bt_kernel<",
                "ffn_down": "gemm_bt_kernel<"}.get(kind)
-    for name, t in rec.get("kernels", {}).items():
+    for name, t in rec.items():
         if not (pattern and pattern in name):
             continue
         if kind.startswith(("fwd", "bwd", "decode")) and not (f"<{head_dim}," in name or f"<{head_dim}>" in name):
@@ -402,7 +405,7 @@ def kernel_sources(name: str):
 REF_COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_mib: int):
+def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_mib: int, workload: str):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters read
     for the reference copy of known size, average per kernel, write profiles/traffic.json
     (with the kernel sources' hashes) and print markdown tables of both passes."""
@@ -447,13 +450,14 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
     csrc = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
-    known = rec.get("kernels", {})
-    for name, t in kernels.items():
-        known[name] = dict(t, source_sha256={f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
-                                             for f in kernel_sources(name)})
-    rec = {"kernels": known,
-           "note": "HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; an entry is "
-                   "stale once any source file listed with it has changed"}
+    workloads = rec.get("workloads", {})
+    workloads[workload] = {
+        name: dict(t, source_sha256={f: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+                                     for f in kernel_sources(name)})
+        for name, t in kernels.items()}
+    rec = {"workloads": workloads,
+           "note": "per workload: HBM bytes per dispatch from FETCH_SIZE/WRITE_SIZE, scaled by a reference copy; "
+                   "an entry is stale once any source file listed with it has changed"}
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     rows = list(csv.DictReader(open(stats_csv)))
@@ -467,7 +471,7 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
 def main():
     args = parse()
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, args.copy_ref_mib)
+        summarize_profiles(*args.summarize_profiles, args.copy_ref_mib, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
@@ -578,7 +582,7 @@ def main():
     achieved = alg[dom] / (dom_ms * 1e-3) / 1e12 if dom in kern else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": (achieved / peak) if achieved else None,
-                "traffic": profiled_traffic(dom, d, w.dtype)}
+                "traffic": profiled_traffic(dom, d, w.dtype, w.name)}
 
     overlap = {"copy_ms_per_step": copy_ms / args.steps, "hidden_ms_per_step": hidden_ms / args.steps,
                "hidden_frac": (hidden_ms / copy_ms) if copy_ms > 0 else None,
