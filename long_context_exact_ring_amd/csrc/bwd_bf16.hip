@@ -431,7 +431,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
 #define RA_BWD_BR 32
 #endif
 #ifndef RA_BWD_BC
-#define RA_BWD_BC 32
+#define RA_BWD_BC 64  // dQ kernel: keys per tile (64 measured 5% faster than 32)
 #endif
 
 template <int D>
