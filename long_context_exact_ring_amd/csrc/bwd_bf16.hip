@@ -42,7 +42,10 @@ namespace {
 #define RA_KV_KLDS 1
 #endif
 #ifndef RA_KV_LAG
-#define RA_KV_LAG 1
+#define RA_KV_LAG 0  // 1: second wave per SIMD half a tile behind (+1% alone, -1% with RA_KV_PAIR)
+#endif
+#ifndef RA_KV_PAIR
+#define RA_KV_PAIR 1  // one barrier per two query tiles (+1.7% on dK/dV)
 #endif
 constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
 constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per SIMD; K rows read from LDS)
@@ -55,7 +58,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BR * ROWB;
   constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
-  constexpr int NB = LAG ? 3 : 2;                 // LDS stages
+  // LDS stages.  PAIR: one barrier per two query tiles, the DMA of the next
+  // two tiles issued right after it (two more stages).
+  constexpr bool PAIR = RA_KV_PAIR != 0;
+  constexpr int NB = (LAG ? 3 : 2) + (PAIR ? 2 : 0);
   constexpr int KTB = KLDS ? NW * 32 * ROWB : 16;  // the workgroup's K rows (KLDS: read from LDS)
   static_assert(BR % 32 == 0 && (BR == 32 || BR % 64 == 0), "row-term DMA covers 64 dwords per wave");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NB * STAGE];
@@ -210,10 +216,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     BF pfl[BR / 32][2], sfl[BR / 32][2];
     int cur = 0;  // stage of tile it
     auto step = [&](int it, auto masked_tag) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` has landed
-      __syncthreads();                                     // ... everyone's; the stage of tile it-NB+1 is free
       const int nxt = cur + 1 == NB ? 0 : cur + 1;
-      if (it + 1 < iters) issue(it + 1, smem + nxt * STAGE);
+      if (!PAIR || (it & 1) == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` (PAIR: and it+1) has landed
+        __syncthreads();  // ... everyone's; every wave is past tile it-1, so the stages of tiles <= it-NB+1 are free
+        if constexpr (PAIR) {
+          if (it + 2 < iters) issue(it + 2, smem + (it + 2) % NB * STAGE);
+          if (it + 3 < iters) issue(it + 3, smem + (it + 3) % NB * STAGE);
+        } else {
+          if (it + 1 < iters) issue(it + 1, smem + nxt * STAGE);
+        }
+      }
       const unsigned char* st = smem + cur * STAGE;
       if constexpr (LAGGED) {
         if (prev_active) part3(smem + (cur == 0 ? NB - 1 : cur - 1) * STAGE, pfl, sfl);
@@ -225,6 +238,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
       cur = nxt;
     };
     if (iters > 0) issue(0, smem);
+    if (PAIR && iters > 1) issue(1, smem + STAGE);
     int it = 0;
     for (int hh = 0; hh < a.group; ++hh) {
       const int base = hh * per_head - qt_lo;  // it = base + qt
