@@ -14,9 +14,10 @@
 // reads (tr_frag) instead of being stored twice; diagonal-band and ragged
 // tiles run in separate (masked) loops so the hot loop carries no masking.
 //
-//  * dK/dV kernel: a wave owns 32 keys (K, V in registers as B operands, keys
-//    on lanes) and walks the query tiles of every query head of its group.
-//    S and dP come out with keys on lanes, so P and dS are B operands of
+//  * dK/dV kernel: a wave owns 32 keys (B operands with keys on lanes: V in
+//    registers, the workgroup's K rows staged in LDS once) and walks the query
+//    tiles of every query head of its group, two tiles per barrier.  S and dP
+//    come out with keys on lanes, so P and dS are B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposed reads
 //    of the streamed Q and dO tiles.  The row terms (lse, Delta) of a tile
 //    ride along in LDS.

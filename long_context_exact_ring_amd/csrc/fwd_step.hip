@@ -15,14 +15,17 @@
 //    serves NW*32 query rows.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16.
 //    The accumulator then keeps one query per lane (16 keys per lane, the other
-//    16 in lane l^32), so the row max needs a single cross-half exchange and the
-//    row sum none until the end.  Q lives in registers as the B operand.
+//    16 in lane l^32), so the row max needs at most one cross-half exchange and
+//    the row sum none until the end.  Q lives in registers as the B operand.
 //  * The exponentiated tile P^T is fed back unchanged as the B operand of
-//    O^T += V^T P^T.  To make that legal V^T is staged in LDS with its keys
-//    permuted inside every 16-key chunk to the order in which the accumulator
-//    holds them (perm_pos); the contraction over keys is order-free.
-//  * K/V tiles are double-buffered in LDS: the next tile's global loads are in
-//    flight in registers while the current tile is computed; one barrier per tile.
+//    O^T += V^T P^T.  To make that legal the V operand takes its keys in the
+//    order in which the accumulator holds them (the contraction over keys is
+//    order-free): the fp32 path stages V^T in LDS with the keys of every
+//    16-key chunk permuted (perm_pos); the bf16 path keeps V in its natural
+//    layout and reads it transposed in that order.
+//  * K/V tiles are double-buffered in LDS with one barrier per tile: the bf16
+//    path copies the next tile global -> LDS by LDS DMA while the current one
+//    is computed; the fp32 path stages it through registers.
 //  * Causal (diagonal block): tiles wholly above a wave's rows are skipped, the
 //    straddling tile is masked; heavy row tiles are dispatched first.
 //  * Epilogue: normalise, then overwrite (first round) or merge into the running
