@@ -53,6 +53,11 @@ def parse():
                    help="no GPU work: turn rocprofv3 CSV output (kernel stats, FETCH_SIZE pass, WRITE_SIZE "
                         "pass, all taken with --copy-ref-mib on the workload named by --workload) into "
                         "profiles/traffic.json and print the summary tables")
+    p.add_argument("--summarize-mfma", metavar="PMC_CSV",
+                   help="no GPU work: matrix-core busy fraction and wave wait/issue shares per kernel from a "
+                        "rocprofv3 --pmc pass of SQ counters")
+    p.add_argument("--summarize-overlap", nargs=2, metavar=("KERNEL_TRACE_CSV", "MEMORY_COPY_TRACE_CSV"),
+                   help="no GPU work: share of the device-to-device copy time hidden under kernels")
     return p.parse_args()
 
 
@@ -434,18 +439,21 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
     fetch, ref_f = per_kernel(fetch_csv)
     write, ref_w = per_kernel(write_csv)
     sf, sw = ref_kib / ref_f, ref_kib / ref_w
+    rows = list(csv.DictReader(open(stats_csv)))
+    avg_ns = {row["Name"].split("(")[0].replace("void ", ""): float(row["AverageNs"]) for row in rows}
     kernels = {}
     print(f"Scaling: the {copy_ref_mib} MiB reference copy ({ref_kib:.0f} KiB read + {ref_kib:.0f} KiB "
           f"written) reads FETCH_SIZE = {ref_f:.0f} KiB and WRITE_SIZE = {ref_w:.0f} KiB, so FETCH_SIZE is "
           f"scaled by {sf:.3f} and WRITE_SIZE by {sw:.3f}.\n")
     print("| kernel | dispatches | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | read (MB, scaled) | "
-          "written (MB, scaled) |")
-    print("|---|---|---|---|---|---|")
+          "written (MB, scaled) | HBM GB/s (at the trace's average duration) |")
+    print("|---|---|---|---|---|---|---|")
     for name in sorted(set(fetch) & set(write)):
         (f, n), (wv, _) = fetch[name], write[name]
         rb, wb = f * sf * 1024.0, wv * sw * 1024.0
         kernels[name] = {"read_bytes": rb, "write_bytes": wb}
-        print(f"| `{name}` | {n} | {f:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        gbs = f"{(rb + wb) / avg_ns[name]:.0f}" if avg_ns.get(name) else "-"
+        print(f"| `{name}` | {n} | {f:.0f} | {wv:.0f} | {rb / 1e6:.1f} | {wb / 1e6:.1f} | {gbs} |")
     # merge into the committed record; every kernel entry carries the source hashes it was taken with
     csrc = os.path.join(ROOT, "long_context_exact_ring_amd", "csrc")
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -460,7 +468,6 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
                    "an entry is stale once any source file listed with it has changed"}
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
-    rows = list(csv.DictReader(open(stats_csv)))
     print("\n| kernel | calls | avg (us) | total (ms) | % of kernel time |")
     print("|---|---|---|---|---|")
     for row in rows:
@@ -468,10 +475,76 @@ def summarize_profiles(stats_csv: str, fetch_csv: str, write_csv: str, copy_ref_
               f"{float(row['TotalDurationNs']) / 1e6:.1f} | {row['Percentage']} |")
 
 
+def summarize_mfma(pmc_csv: str):
+    """Matrix-core utilisation per kernel from one rocprofv3 --pmc pass of SQ counters.
+
+    busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES): the register-only MFMA
+    loop (ring_attn_mfma_rate, also in the run) reads 1.00 with it.  The wave-cycle
+    shares come from SQ_WAIT_ANY, SQ_ACTIVE_INST_ANY and SQ_WAVE_CYCLES."""
+    import collections
+    import csv
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for row in csv.DictReader(open(pmc_csv)):
+        name = row["Kernel_Name"].split("(")[0].replace("void ", "")
+        acc[name][row["Counter_Name"]] += float(row["Counter_Value"])
+        disp[name].add(row["Dispatch_Id"])
+    print("| kernel | dispatches | MFMA busy | waves waiting (SQ_WAIT_ANY) | waves issuing (SQ_ACTIVE_INST_ANY) | "
+          "LDS bank conflicts per LDS instruction |")
+    print("|---|---|---|---|---|---|")
+    for name in sorted(acc):
+        c = acc[name]
+        if not c.get("SQ_BUSY_CU_CYCLES"):
+            continue
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (4.0 * c["SQ_BUSY_CU_CYCLES"])
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        wait = f"{c['SQ_WAIT_ANY'] / wc:.2f}" if wc and "SQ_WAIT_ANY" in c else "-"
+        act = f"{c['SQ_ACTIVE_INST_ANY'] / wc:.2f}" if wc and "SQ_ACTIVE_INST_ANY" in c else "-"
+        lds = c.get("SQ_INSTS_LDS", 0.0)
+        conf = f"{c['SQ_LDS_BANK_CONFLICT'] / lds:.3f}" if lds and "SQ_LDS_BANK_CONFLICT" in c else "-"
+        print(f"| `{name}` | {len(disp[name])} | {busy:.2f} | {wait} | {act} | {conf} |")
+
+
+def summarize_overlap(kernel_trace_csv: str, copy_trace_csv: str):
+    """Share of the device-to-device copy time during which some kernel was running, from
+    a rocprofv3 --kernel-trace --memory-copy-trace run (the K/V rotation copies)."""
+    import csv
+    spans = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in csv.DictReader(open(kernel_trace_csv)))
+    merged = []
+    for a, b in spans:
+        if merged and a <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], b)
+        else:
+            merged.append([a, b])
+    copies = [r for r in csv.DictReader(open(copy_trace_csv))
+              if any("DEVICE_TO_DEVICE" in str(v) for v in r.values())]
+    import bisect
+    starts = [m[0] for m in merged]
+    total = hidden = 0
+    for r in copies:
+        a, b = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        total += b - a
+        i = max(bisect.bisect_right(starts, a) - 1, 0)
+        while i < len(merged) and merged[i][0] < b:
+            lo, hi = max(a, merged[i][0]), min(b, merged[i][1])
+            if hi > lo:
+                hidden += hi - lo
+            i += 1
+    print(f"device-to-device copies: {len(copies)}, {total / 1e6:.1f} ms in total, "
+          f"{hidden / 1e6:.1f} ms of it while a kernel ran: hidden fraction {hidden / max(total, 1):.4f}")
+    return hidden / max(total, 1)
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.copy_ref_mib, args.workload)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
+        return
+    if args.summarize_overlap:
+        summarize_overlap(*args.summarize_overlap)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
