@@ -1,6 +1,7 @@
 """CPU checks of bench.py's host logic: the profiler-summary bookkeeping that
 feeds `roofline.traffic` (scaling by the reference copy, per-workload records,
-staleness by source hash) and the single-GPU guard.  No GPU is touched.
+staleness by source hash), the matrix-core and copy-overlap summaries, and the
+single-GPU guard.  No GPU is touched.
 """
 import csv
 import json
@@ -104,3 +105,39 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_mfma_busy_is_normalised_to_four_simds(tmp_path, capsys):
+    path = tmp_path / "sq.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, (k, busy_cu, mfma) in enumerate((("ra::mfma_rate_kernel(int, float*)", 100.0, 400.0),
+                                                ("void ra::fwd_bf16_kernel<128, 64, 8, 1>(ra::FwdArgs)", 100.0, 200.0))):
+            for c, v in (("SQ_BUSY_CU_CYCLES", busy_cu), ("SQ_VALU_MFMA_BUSY_CYCLES", mfma), ("SQ_WAVE_CYCLES", 1000.0),
+                         ("SQ_WAIT_ANY", 400.0), ("SQ_ACTIVE_INST_ANY", 300.0)):
+                w.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+    bench.summarize_mfma(str(path))
+    out = capsys.readouterr().out
+    assert "| `ra::mfma_rate_kernel` | 1 | 1.00 | 0.40 | 0.30 |" in out
+    assert "| `ra::fwd_bf16_kernel<128, 64, 8, 1>` | 1 | 0.50 |" in out
+
+
+def test_copy_overlap_counts_only_device_copies_under_kernels(tmp_path, capsys):
+    kern = tmp_path / "k.csv"
+    with open(kern, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for a, b in ((0, 100), (50, 150), (300, 400)):  # union: [0,150) and [300,400)
+            w.writerow({"Kernel_Name": "k", "Start_Timestamp": a, "End_Timestamp": b})
+    copy = tmp_path / "c.csv"
+    with open(copy, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Direction", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerow({"Direction": "MEMORY_COPY_DEVICE_TO_DEVICE", "Start_Timestamp": 100, "End_Timestamp": 200})
+        w.writerow({"Direction": "MEMORY_COPY_DEVICE_TO_DEVICE", "Start_Timestamp": 250, "End_Timestamp": 350})
+        w.writerow({"Direction": "MEMORY_COPY_HOST_TO_DEVICE", "Start_Timestamp": 500, "End_Timestamp": 900})
+    frac = bench.summarize_overlap(str(kern), str(copy))
+    capsys.readouterr()
+    # copy 1: [100,150) under kernels of 100; copy 2: [300,350) of 100 -> 100 of 200
+    assert frac == pytest.approx(0.5)
