@@ -25,6 +25,7 @@ CASES = [
     (128, 2, 2, 33, 5, 3, 0),          # first positions: row 0 sees one key, later rows a few
     (128, 16, 1, 256, 1, 2, "end"),    # group 16 x 2 rows = 32, a ring of one
     (64, 2, 2, 5000, 2, 1, 7777),      # long blocks, cut inside block 1
+    (128, 8, 2, 64, 64, 2, 3000),      # the most blocks one call takes (64), cut inside block 46
 ]
 
 

@@ -71,3 +71,19 @@ def test_full_ffn_block_sampled_rows():
                                      np.random.default_rng(0).integers(0, w.rows, 8)]))
     ref = oracle.ffn_forward(x[rows], w1, b1, w2, b2)
     compare("y (sampled rows)", y[torch.from_numpy(rows).cuda()], ref, "bf16")
+
+
+def test_large_tiles_match_small_tiles_bit_for_bit():
+    """4096 rows x 4096 hidden x 4096 ffn: as one block both GEMMs take the 256x256
+    workgroup tiles; in 1024-row chunks they take the 128x128 ones.  Every output
+    element is accumulated over k in the same order either way, so the two must agree
+    bit for bit; sampled rows are also checked against the oracle."""
+    require_gpu()
+    x, w1, b1, w2, b2 = _inputs(103, 4096, 4096, 4096, True)
+    y_big = _run(x, w1, b1, w2, b2, 0)
+    y_small = _run(x, w1, b1, w2, b2, 1024)
+    torch.cuda.synchronize()
+    assert torch.equal(y_big, y_small)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095], np.random.default_rng(1).integers(0, 4096, 6)]))
+    compare("y (sampled rows)", y_big[torch.from_numpy(rows).cuda()], oracle.ffn_forward(x[rows], w1, b1, w2, b2),
+            "bf16")
