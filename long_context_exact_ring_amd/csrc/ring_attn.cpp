@@ -666,7 +666,7 @@ int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
 }
 
 #ifndef RA_DEC_WAVES
-#define RA_DEC_WAVES 2048
+#define RA_DEC_WAVES 1024
 #endif
 
 int decode_impl(const void* q, const void* const* kb, const void* const* vb, int n_blocks, int block_len,
@@ -701,9 +701,11 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
       if (overlaps(outs[o], ob[o], kb[j], kvb) || overlaps(outs[o], ob[o], vb[j], kvb))
         return fail(RA_ERR_INVALID_ARG, "%s overlaps K/V block %d", o ? "lse" : "out", j);
   }
-  // keys per wave: about RA_DEC_WAVES waves over the whole context, 256..8192 keys each
+  // keys per wave: about RA_DEC_WAVES waves over the whole context, rounded to a power of
+  // two (so that power-of-two blocks split without a short last chunk), 256..8192 keys each
   const double total = (double)n_blocks * kv_heads * block_len;
-  int chunk = (int)std::min(8192.0, std::max(256.0, std::ceil(total / (double)RA_DEC_WAVES / 32.0) * 32.0));
+  const double target = std::max(256.0, std::min(8192.0, total / (double)RA_DEC_WAVES));
+  const int chunk = 1 << (int)std::lround(std::log2(target));
   const int n_chunks = (block_len + chunk - 1) / chunk;
   const int rows = group * q_len;
   const size_t n_parts = (size_t)n_blocks * n_chunks;
