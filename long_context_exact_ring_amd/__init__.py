@@ -95,11 +95,18 @@ def lib() -> ctypes.CDLL:
 
 # ------------------------------------------------------------------ marshalling helpers
 def _addr(x) -> Optional[int]:
-    """Device address of a tensor (or a raw integer address / None)."""
+    """Device address of a tensor (or a raw integer address / None).
+
+    The library reads every buffer as a dense row-major array, so a tensor must live
+    on the GPU and be contiguous; views with other strides are refused here."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got strides {tuple(x.stride())} for shape {tuple(x.shape)}")
     return x.data_ptr()
 
 

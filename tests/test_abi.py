@@ -193,3 +193,9 @@ def test_ffn_validation_before_any_hip_call():
     assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 200, 0, y, None) == ra.RA_ERR_UNSUPPORTED
     assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 256, -1, y, None) == ra.RA_ERR_INVALID_ARG
     assert L.ring_attn_ffn_blockwise(x, w1, None, w2, None, 8, 128, 256, 0, x + 64, None) == ra.RA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ra._addr(torch.zeros(4))

@@ -235,3 +235,12 @@ def test_mfma_rate_probe_is_plausible():
     log(f"  mfma loop: {tf:.1f} TFLOP/s")
     assert 300.0 < tf < 2600.0  # below the public dense bf16 figure, far above any scalar path
     assert torch.isfinite(sink).all()
+
+
+def test_binding_refuses_strided_views():
+    """The library reads dense row-major buffers; a transposed view must be refused, not misread."""
+    require_gpu()
+    q = torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    kb = [torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")]
+    with pytest.raises(ValueError, match="contiguous"):
+        ra.fwd(q.transpose(0, 1), kb, kb, causal=False, rank=0)
