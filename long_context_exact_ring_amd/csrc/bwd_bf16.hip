@@ -55,7 +55,7 @@ constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per S
 
 // =================================================================== dK / dV
 template <int D, int BR, int NW, bool KLDS, bool LAG>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BR * ROWB;
   constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
@@ -279,9 +279,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
 }
 
+template <int D, int BR, int NW, bool KLDS, bool LAG>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
+  dkdv_body<D, BR, NW, KLDS, LAG>(a);
+}
+// Two independent dK/dV sub-problems of one launch (blockIdx.y selects), e.g. the
+// zig-zag layout's two key chunks of a block against the same query chunk.
+template <int D, int BR, int NW, bool KLDS, bool LAG>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_pair_kernel(ArgPair<BwdArgs> pair) {
+  const BwdArgs a = pair.s[blockIdx.y];
+  dkdv_body<D, BR, NW, KLDS, LAG>(a);
+}
+
 // =================================================================== dQ
 template <int D, int BC, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+__device__ __forceinline__ void dq_body(const BwdArgs& a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
   constexpr int STAGE = 2 * TILEB;  // K tile, V tile
@@ -442,6 +454,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
     }
 }
 
+template <int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+  dq_body<D, BC, NW>(a);
+}
+// Two independent dQ sub-problems of one launch (blockIdx.y selects), e.g. the
+// zig-zag layout's two query chunks against the same key chunk of a block.
+template <int D, int BC, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_pair_kernel(ArgPair<BwdArgs> pair) {
+  const BwdArgs a = pair.s[blockIdx.y];
+  dq_body<D, BC, NW>(a);
+}
+
 #ifndef RA_BWD_BR
 #define RA_BWD_BR 32
 #endif
@@ -450,35 +474,46 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
 #endif
 
 template <int D>
-static hipError_t launch_dkdv_bf16_t(const BwdArgs& a, hipStream_t st) {
+static hipError_t launch_dkdv_bf16_t(const BwdArgs* a, int nsub, hipStream_t st) {
   const int KW = kKvNW * 32;
-  const int nblk = ((a.len + KW - 1) / KW) * a.hkv;
+  const int nblk = ((a[0].len + KW - 1) / KW) * a[0].hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>), dim3(nblk),
-                     dim3(kKvNW * 64), 0,
-                     st, a);
+  ArgPair<BwdArgs> pair{};
+  for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];
+  if (nsub == 1)
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>), dim3(nblk),
+                       dim3(kKvNW * 64), 0, st, a[0]);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_bf16_pair_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>),
+                       dim3(nblk, nsub), dim3(kKvNW * 64), 0, st, pair);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_dq_bf16_t(const BwdArgs& a, hipStream_t st) {
-  if (a.hpw < 1 || a.hsub < 1 || kBwdNW % a.hpw != 0) return hipErrorInvalidValue;
-  const int R = kBwdNW * 32 / a.hpw;
-  const int nblk = ((a.len + R - 1) / R) * a.hsub * a.hkv;
+static hipError_t launch_dq_bf16_t(const BwdArgs* a, int nsub, hipStream_t st) {
+  if (a[0].hpw < 1 || a[0].hsub < 1 || kBwdNW % a[0].hpw != 0) return hipErrorInvalidValue;
+  const int R = kBwdNW * 32 / a[0].hpw;
+  const int nblk = ((a[0].len + R - 1) / R) * a[0].hsub * a[0].hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, RA_BWD_BC, kBwdNW>), dim3(nblk), dim3(kBwdNW * 64), 0, st, a);
+  ArgPair<BwdArgs> pair{};
+  for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];
+  if (nsub == 1)
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, RA_BWD_BC, kBwdNW>), dim3(nblk), dim3(kBwdNW * 64), 0, st, a[0]);
+  else
+    hipLaunchKernelGGL((bwd_dq_bf16_pair_kernel<D, RA_BWD_BC, kBwdNW>), dim3(nblk, nsub), dim3(kBwdNW * 64), 0, st,
+                       pair);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t st) {
-  if (head_dim == 64) return launch_dkdv_bf16_t<64>(a, st);
-  if (head_dim == 128) return launch_dkdv_bf16_t<128>(a, st);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs* a, int nsub, int head_dim, hipStream_t st) {
+  if (head_dim == 64) return launch_dkdv_bf16_t<64>(a, nsub, st);
+  if (head_dim == 128) return launch_dkdv_bf16_t<128>(a, nsub, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int head_dim, hipStream_t st) {
-  if (head_dim == 64) return launch_dq_bf16_t<64>(a, st);
-  if (head_dim == 128) return launch_dq_bf16_t<128>(a, st);
+hipError_t launch_bwd_dq_bf16(const BwdArgs* a, int nsub, int head_dim, hipStream_t st) {
+  if (head_dim == 64) return launch_dq_bf16_t<64>(a, nsub, st);
+  if (head_dim == 128) return launch_dq_bf16_t<128>(a, nsub, st);
   return hipErrorInvalidValue;
 }
 

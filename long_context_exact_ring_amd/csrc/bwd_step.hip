@@ -359,8 +359,20 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
-  if (elem_bytes == 2) return launch_bwd_dkdv_bf16(a, head_dim, st);
+// sub-problems of one launch must agree on the grid: same length and head layout
+static bool same_bwd_grid(const BwdArgs* a, int nsub) {
+  for (int i = 1; i < nsub; ++i)
+    if (a[i].len != a[0].len || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv || a[i].hpw != a[0].hpw ||
+        a[i].hsub != a[0].hsub)
+      return false;
+  return true;
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
+  if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
+  if (elem_bytes == 2) return launch_bwd_dkdv_bf16(ap, nsub, head_dim, st);
+  if (nsub != 1) return hipErrorInvalidValue;  // the fp32 path runs one sub-problem per launch
+  const BwdArgs& a = ap[0];
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dkdv_t<bf16_storage, 64, 32>(a, st);
     if (head_dim == 128) return launch_dkdv_t<bf16_storage, 128, RA_KV_BR>(a, st);
@@ -371,8 +383,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipSt
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
-  if (elem_bytes == 2) return launch_bwd_dq_bf16(a, head_dim, st);
+hipError_t launch_bwd_dq(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
+  if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
+  if (elem_bytes == 2) return launch_bwd_dq_bf16(ap, nsub, head_dim, st);
+  if (nsub != 1) return hipErrorInvalidValue;
+  const BwdArgs& a = ap[0];
   if (elem_bytes == 2) {
     if (head_dim == 64) return launch_dq_t<bf16_storage, 64, 32>(a, st);
     if (head_dim == 128) return launch_dq_t<bf16_storage, 128, RA_DQ_BC>(a, st);

@@ -308,8 +308,16 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
     }
 }
 
-template <int D, int BC, int NW, int RG>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+// The arguments of this workgroup's sub-problem: a single argument set, or the
+// blockIdx.y entry of a pair (the kernel is instantiated for both; unlike the
+// backward's body-plus-wrapper kernels, this form keeps the single-argument
+// forward's code exactly as fast as a plain FwdArgs kernel -- measured).
+__device__ __forceinline__ const FwdArgs& fwd_sub_args(const FwdArgs& a) { return a; }
+__device__ __forceinline__ FwdArgs fwd_sub_args(const ArgPair<FwdArgs>& p) { return p.s[blockIdx.y]; }
+
+template <int D, int BC, int NW, int RG, typename ARG>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(ARG arg) {
+  const FwdArgs a = fwd_sub_args(arg);  // ARG: FwdArgs, or a pair of them along gridDim.y
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BC * ROWB;
   constexpr int STAGE = 2 * TILEB;
@@ -460,23 +468,40 @@ constexpr int kF32Waves = kFwdWaves;
 #define RA_FWD_RG 1  // 32-row query groups per wave (2: 64 rows at one wave per SIMD)
 #endif
 
+// sub-problems of one launch must agree on the grid: same length and head layout
+template <typename A> static bool same_grid(const A* a, int nsub) {
+  for (int i = 1; i < nsub; ++i)
+    if (a[i].len != a[0].len || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv || a[i].hpw != a[0].hpw ||
+        a[i].hsub != a[0].hsub)
+      return false;
+  return true;
+}
+
 template <int D, int BC, int NW>
-static hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-  if (a.hpw < 1 || a.hsub < 1 || NW % a.hpw != 0) return hipErrorInvalidValue;
-  const int R = NW * 32 * RA_FWD_RG / a.hpw;
-  const int nblk = ((a.len + R - 1) / R) * a.hsub * a.hkv;
+static hipError_t launch_fwd_bf16(const FwdArgs* a, int nsub, hipStream_t st) {
+  if (a[0].hpw < 1 || a[0].hsub < 1 || NW % a[0].hpw != 0) return hipErrorInvalidValue;
+  const int R = NW * 32 * RA_FWD_RG / a[0].hpw;
+  const int nblk = ((a[0].len + R - 1) / R) * a[0].hsub * a[0].hkv;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RA_FWD_RG>), dim3(nblk), dim3(NW * 64), 0, st, a);
+  ArgPair<FwdArgs> pair{};
+  for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];
+  if (nsub == 1)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RA_FWD_RG, FwdArgs>), dim3(nblk), dim3(NW * 64), 0, st, a[0]);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, RA_FWD_RG, ArgPair<FwdArgs>>), dim3(nblk, nsub), dim3(NW * 64), 0,
+                       st, pair);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st) {
+hipError_t launch_fwd_step(const FwdArgs* a, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
+  if (nsub < 1 || nsub > 2 || !same_grid(a, nsub)) return hipErrorInvalidValue;
   if (elem_bytes == 2) {
-    if (head_dim == 64) return launch_fwd_bf16<64, RA_FWD_BC, kFwdWaves>(a, st);
-    if (head_dim == 128) return launch_fwd_bf16<128, RA_FWD_BC, kFwdWaves>(a, st);
+    if (head_dim == 64) return launch_fwd_bf16<64, RA_FWD_BC, kFwdWaves>(a, nsub, st);
+    if (head_dim == 128) return launch_fwd_bf16<128, RA_FWD_BC, kFwdWaves>(a, nsub, st);
   } else {
-    if (head_dim == 64) return launch_fwd_t<float, 64, 64, kF32Waves>(a, st);
-    if (head_dim == 128) return launch_fwd_t<float, 128, 32, kF32Waves>(a, st);
+    if (nsub != 1) return hipErrorInvalidValue;  // the fp32 path runs one sub-problem per launch
+    if (head_dim == 64) return launch_fwd_t<float, 64, 64, kF32Waves>(a[0], st);
+    if (head_dim == 128) return launch_fwd_t<float, 128, 32, kF32Waves>(a[0], st);
   }
   return hipErrorInvalidValue;
 }

@@ -23,7 +23,13 @@ struct FwdArgs {
   int ls;       // elements between heads in lse (len, or more when rows are a slice of a longer block)
 };
 
-hipError_t launch_fwd_step(const FwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+// Up to two independent sub-problems share one launch along gridDim.y (the
+// zig-zag layout's two query chunks for the forward and dQ, or two key chunks
+// for dK/dV); the bf16 path has a pair variant of each kernel, in which every
+// workgroup runs the sub-problem of its blockIdx.y.
+template <typename A> struct ArgPair { A s[2]; };
+
+hipError_t launch_fwd_step(const FwdArgs* a, int nsub, int elem_bytes, int head_dim, hipStream_t st);
 // waves per forward workgroup for an element size (the host packs heads by it)
 int fwd_waves_per_block(int elem_bytes);
 
@@ -59,12 +65,12 @@ struct BwdArgs {
   float scale_log2;  // log2(e)/sqrt(D)
   int ls;            // elements between heads in lse / delta / lse2
 };
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
-hipError_t launch_bwd_dq(const BwdArgs& a, int elem_bytes, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dkdv(const BwdArgs* a, int nsub, int elem_bytes, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dq(const BwdArgs* a, int nsub, int elem_bytes, int head_dim, hipStream_t st);
 int bwd_dq_waves_per_block();
 // bf16 fast paths (LDS-DMA staging, transposed operand reads)
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t st);
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs* a, int nsub, int head_dim, hipStream_t st);
+hipError_t launch_bwd_dq_bf16(const BwdArgs* a, int nsub, int head_dim, hipStream_t st);
 int bwd_bf16_waves_per_block();
 
 // Pairwise merge of two normalised partials.

@@ -415,16 +415,21 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
       a.first = (s == 0) ? 1 : 0;
       ProfScope ps(KIND_FWD, stream);
-      RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
+      RA_HIP(launch_fwd_step(&a, 1, sh.elem_bytes, sh.head_dim, stream));
       return RA_OK;
     }
-    // zig-zag: query half u holds chunk zz_chunk(rank, u), key half v chunk zz_chunk(j, v)
+    // zig-zag: query half u holds chunk zz_chunk(rank, u), key half v chunk zz_chunk(j, v).
+    // For each key half, the query halves that see it run as the two sub-problems of
+    // one launch (they write different rows); the key halves follow one another.
     const int h = sh.block_len / 2;
-    for (int u = 0; u < 2; ++u)
-      for (int v = 0; v < 2; ++v) {
+    for (int v = 0; v < 2; ++v) {
+      FwdArgs sub[2];
+      int nsub = 0;
+      for (int u = 0; u < 2; ++u) {
         const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
         if (sh.causal && kc > qc) continue;  // every key of the chunk lies in the queries' future
-        FwdArgs a = base;
+        FwdArgs& a = sub[nsub++];
+        a = base;
         a.q = static_cast<const char*>(q) + (size_t)u * h * sh.heads * sh.head_dim * sh.elem_bytes;
         a.out = out + (size_t)u * h * sh.heads * sh.head_dim;
         a.lse = lse + (size_t)u * h;
@@ -434,9 +439,11 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
         a.diag = (sh.causal && kc == qc) ? 1 : 0;
         a.first = first_half[u] ? 1 : 0;
         first_half[u] = false;
-        ProfScope ps(KIND_FWD, stream);
-        RA_HIP(launch_fwd_step(a, sh.elem_bytes, sh.head_dim, stream));
       }
+      if (nsub == 0) continue;
+      ProfScope ps(KIND_FWD, stream);
+      RA_HIP(launch_fwd_step(sub, nsub, sh.elem_bytes, sh.head_dim, stream));
+    }
     return RA_OK;
   };
   return run_ring(c, sh, kb, vb, stream, step);
@@ -511,15 +518,14 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   base.hsub = group / hpw;
   base.scale = scale;
   base.scale_log2 = 1.4426950408889634f * scale;
-  auto launch_pair = [&](const BwdArgs& a) -> int {
-    {
-      ProfScope ps(KIND_DKDV, stream);
-      RA_HIP(launch_bwd_dkdv(a, sh.elem_bytes, sh.head_dim, stream));
-    }
-    {
-      ProfScope ps(KIND_DQ, stream);
-      RA_HIP(launch_bwd_dq(a, sh.elem_bytes, sh.head_dim, stream));
-    }
+  auto launch_dkdv = [&](const BwdArgs* a, int nsub) -> int {
+    ProfScope ps(KIND_DKDV, stream);
+    RA_HIP(launch_bwd_dkdv(a, nsub, sh.elem_bytes, sh.head_dim, stream));
+    return RA_OK;
+  };
+  auto launch_dq = [&](const BwdArgs* a, int nsub) -> int {
+    ProfScope ps(KIND_DQ, stream);
+    RA_HIP(launch_bwd_dq(a, nsub, sh.elem_bytes, sh.head_dim, stream));
     return RA_OK;
   };
   bool first_half[2] = {true, true};
@@ -532,15 +538,22 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       a.dv = dvb[j];
       a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
       a.first = (s == 0) ? 1 : 0;
-      return launch_pair(a);
+      int st2 = launch_dkdv(&a, 1);
+      return st2 != RA_OK ? st2 : launch_dq(&a, 1);
     }
+    // zig-zag: the (query half u, key half v) pairs that attend.  dK/dV launches take the
+    // key halves of one query half as two sub-problems (they write different dK/dV rows);
+    // dQ launches take the query halves of one key half (different dQ rows).
     const int h = sh.block_len / 2;
     const size_t qrow = (size_t)sh.heads * sh.head_dim, krow = (size_t)sh.kv_heads * sh.head_dim;
+    BwdArgs pa[2][2];
+    bool live[2][2];
     for (int u = 0; u < 2; ++u)
       for (int v = 0; v < 2; ++v) {
         const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
-        if (sh.causal && kc > qc) continue;
-        BwdArgs a = base;
+        live[u][v] = !(sh.causal && kc > qc);
+        BwdArgs& a = pa[u][v];
+        a = base;
         a.q = static_cast<const char*>(q) + u * h * qrow * sh.elem_bytes;
         a.dout = static_cast<const char*>(dout) + u * h * qrow * sh.elem_bytes;
         a.lse = lse + (size_t)u * h;
@@ -553,11 +566,30 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
         a.dv = dvb[j] + v * h * krow;
         a.len = h;
         a.diag = (sh.causal && kc == qc) ? 1 : 0;
-        a.first = first_half[u] ? 1 : 0;
-        first_half[u] = false;
-        int st2 = launch_pair(a);
-        if (st2 != RA_OK) return st2;
       }
+    for (int u = 0; u < 2; ++u) {
+      BwdArgs sub[2];
+      int nsub = 0;
+      for (int v = 0; v < 2; ++v)
+        if (live[u][v]) sub[nsub++] = pa[u][v];
+      if (nsub == 0) continue;
+      int st2 = launch_dkdv(sub, nsub);
+      if (st2 != RA_OK) return st2;
+    }
+    for (int v = 0; v < 2; ++v) {
+      BwdArgs sub[2];
+      int nsub = 0;
+      for (int u = 0; u < 2; ++u)
+        if (live[u][v]) {
+          BwdArgs& a = sub[nsub++];
+          a = pa[u][v];
+          a.first = first_half[u] ? 1 : 0;  // dQ rows of half u: written by the first, then accumulated
+          first_half[u] = false;
+        }
+      if (nsub == 0) continue;
+      int st2 = launch_dq(sub, nsub);
+      if (st2 != RA_OK) return st2;
+    }
     return RA_OK;
   };
   return run_ring(c, sh, kb, vb, stream, step);

@@ -99,8 +99,17 @@ def test_zigzag_every_rank_runs_the_same_steps():
             ra.ring_attn_profile_enable(False)
         counts.append(recs["fwd_step"][1])
     log(f"  half-size forward launches per rank: {counts}")
-    # the diagonal round runs 3 chunk pairs, every other round 2
-    assert counts == [2 * D + 1] * D
+    # Chunk pairs (query chunk qc, key chunk kc) that attend: kc <= qc.  Block b holds chunks
+    # b and 2D-1-b.  Every rank has 2D+1 of them (3 in its diagonal round, 2 in every other),
+    # and the library launches the query halves that see one key half together.
+    zz = lambda b, half: b if half == 0 else 2 * D - 1 - b
+    pairs, launches = [], []
+    for r in range(D):
+        live = [[zz(j, v) <= zz(r, u) for u in (0, 1) for v in (0, 1)] for j in range(D)]
+        pairs.append(sum(map(sum, live)))
+        launches.append(sum(int(l[0 * 2 + v] or l[1 * 2 + v]) for l in live for v in (0, 1)))
+    assert pairs == [2 * D + 1] * D
+    assert counts == launches
 
 
 def test_zigzag_rejects_odd_block_len():
