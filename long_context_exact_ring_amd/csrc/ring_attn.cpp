@@ -16,6 +16,14 @@
 // "six blocks" of §3.4: Q, O, the K/V in use and the K/V in flight).  With a
 // causal mask the rounds whose block lies in the future are dropped (every
 // rank's own block comes first and is the masked diagonal).
+//
+// In the backward, the dK/dV and dQ kernels of a round read the same K/V
+// block and write different outputs.  With RA_BWD_TWO_STREAMS the dQ chain
+// runs on a second library-owned stream, forked from the main stream at every
+// round: the two kernels of a round share the GPU, and each fills the CUs the
+// other leaves idle while its last workgroups drain.  A staging buffer is then
+// refilled only after both kernels that read it are done, and the main stream
+// joins the dQ chain before the call's work ends.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -32,6 +40,14 @@
 #include "../../include/ring_attn.h"
 #include "kernels.h"
 #include "ring_host.h"
+
+#ifndef RA_BWD_TWO_STREAMS
+// 1: the backward's dQ chain runs on a second stream next to the dK/dV chain
+// (+1.2% on a causal 128k step, +2.2% in the zig-zag layout).  Off: with the
+// two kernels sharing the GPU, each one's event-timed duration spans the
+// other's work too, so per-kernel durations no longer describe the kernels.
+#define RA_BWD_TWO_STREAMS 0
+#endif
 
 namespace ra {
 
@@ -124,6 +140,8 @@ struct Ctx {
   hipStream_t side = nullptr;
   hipEvent_t ev_entry = nullptr, ev_side_end = nullptr;
   hipEvent_t ev_copied[2] = {nullptr, nullptr}, ev_done[2] = {nullptr, nullptr};
+  hipStream_t aux = nullptr;  // backward: the dQ chain
+  hipEvent_t ev_fork[2] = {nullptr, nullptr}, ev_aux_done[2] = {nullptr, nullptr}, ev_aux_end = nullptr;
   void* stage = nullptr;  // [kbuf0 | kbuf1 | vbuf0 | vbuf1]
   size_t stage_cap = 0;
   bool stage_owned = true;  // false: caller memory from ring_attn_set_workspace
@@ -153,8 +171,10 @@ static int get_ctx(Ctx** out) {
   Ctx* c = new Ctx();
   c->device = dev;
   hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
-  hipEvent_t* evs[] = {&c->ev_entry, &c->ev_side_end, &c->ev_copied[0], &c->ev_copied[1], &c->ev_done[0],
-                       &c->ev_done[1]};
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
+  hipEvent_t* evs[] = {&c->ev_entry,   &c->ev_side_end,  &c->ev_copied[0],  &c->ev_copied[1],
+                       &c->ev_done[0], &c->ev_done[1],   &c->ev_fork[0],    &c->ev_fork[1],
+                       &c->ev_aux_done[0], &c->ev_aux_done[1], &c->ev_aux_end};
   for (hipEvent_t* ev : evs)
     if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -307,10 +327,13 @@ static bool log_schedule() {
 }
 
 // ------------------------------------------------------------------ the ring pipeline
-// step_fn(s, j, k_ptr, v_ptr) launches round s's kernels on `stream`.
+// step_fn(s, j, k_ptr, v_ptr) launches round s's kernels on `stream`.  With
+// `aux_done`, step_fn also reads the round's staging buffer from another stream
+// and records aux_done[s & 1] there after its last reader; the buffer is then
+// refilled only after that event as well.
 template <typename StepFn>
 static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* const* vb,
-                    hipStream_t stream, StepFn&& step_fn) {
+                    hipStream_t stream, StepFn&& step_fn, const hipEvent_t* aux_done = nullptr) {
   const std::vector<int> steps = ring_schedule(sh.rank, sh.n_blocks, sh.schedule_causal());
   const int S = (int)steps.size();
   const size_t kvb = sh.kv_bytes();
@@ -355,6 +378,7 @@ static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* 
     if (s + 2 < S) {
       RA_HIP(hipEventRecord(c->ev_done[b], stream));
       RA_HIP(hipStreamWaitEvent(c->side, c->ev_done[b], 0));
+      if (aux_done) RA_HIP(hipStreamWaitEvent(c->side, aux_done[b], 0));
       if ((st = issue_copy(s + 2)) != RA_OK) return st;
     }
   }
@@ -523,13 +547,15 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
     RA_HIP(launch_bwd_dkdv(a, nsub, sh.elem_bytes, sh.head_dim, stream));
     return RA_OK;
   };
+  // the dQ chain runs on c->aux (RA_BWD_TWO_STREAMS), forked from `stream` at every round
+  hipStream_t dq_stream = RA_BWD_TWO_STREAMS ? c->aux : stream;
   auto launch_dq = [&](const BwdArgs* a, int nsub) -> int {
-    ProfScope ps(KIND_DQ, stream);
-    RA_HIP(launch_bwd_dq(a, nsub, sh.elem_bytes, sh.head_dim, stream));
+    ProfScope ps(KIND_DQ, dq_stream);
+    RA_HIP(launch_bwd_dq(a, nsub, sh.elem_bytes, sh.head_dim, dq_stream));
     return RA_OK;
   };
   bool first_half[2] = {true, true};
-  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
+  auto bwd_round = [&](int s, int j, const void* kp, const void* vp) -> int {
     if (!sh.zigzag) {
       BwdArgs a = base;
       a.k = kp;
@@ -592,7 +618,21 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
     }
     return RA_OK;
   };
-  return run_ring(c, sh, kb, vb, stream, step);
+  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
+    if (RA_BWD_TWO_STREAMS) {  // everything enqueued on `stream` so far (copy waits, bwd_pre) precedes this round's dQ
+      RA_HIP(hipEventRecord(c->ev_fork[s & 1], stream));
+      RA_HIP(hipStreamWaitEvent(dq_stream, c->ev_fork[s & 1], 0));
+    }
+    int rc = bwd_round(s, j, kp, vp);
+    if (rc == RA_OK && RA_BWD_TWO_STREAMS) RA_HIP(hipEventRecord(c->ev_aux_done[s & 1], dq_stream));
+    return rc;
+  };
+  int rc = run_ring(c, sh, kb, vb, stream, step, RA_BWD_TWO_STREAMS ? c->ev_aux_done : nullptr);
+  if (rc == RA_OK && RA_BWD_TWO_STREAMS) {
+    RA_HIP(hipEventRecord(c->ev_aux_end, dq_stream));
+    RA_HIP(hipStreamWaitEvent(stream, c->ev_aux_end, 0));
+  }
+  return rc;
 }
 
 int merge_impl(const float* oa, const float* la, const float* obp, const float* lb, int rows, int heads,
@@ -874,11 +914,13 @@ void shutdown_all() {
     if (c->delta) (void)hipFree(c->delta);
     if (c->dec) (void)hipFree(c->dec);
     if (c->ffn) (void)hipFree(c->ffn);
-    hipEvent_t evs[] = {c->ev_entry, c->ev_side_end, c->ev_copied[0], c->ev_copied[1], c->ev_done[0],
-                        c->ev_done[1]};
+    hipEvent_t evs[] = {c->ev_entry,   c->ev_side_end,  c->ev_copied[0],  c->ev_copied[1],
+                        c->ev_done[0], c->ev_done[1],   c->ev_fork[0],    c->ev_fork[1],
+                        c->ev_aux_done[0], c->ev_aux_done[1], c->ev_aux_end};
     for (hipEvent_t e : evs)
       if (e) (void)hipEventDestroy(e);
     if (c->side) (void)hipStreamDestroy(c->side);
+    if (c->aux) (void)hipStreamDestroy(c->aux);
     (void)hipSetDevice(prev);
     delete c;
   }
