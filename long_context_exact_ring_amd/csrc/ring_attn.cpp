@@ -171,12 +171,16 @@ static int get_ctx(Ctx** out) {
   Ctx* c = new Ctx();
   c->device = dev;
   hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
-  hipEvent_t* evs[] = {&c->ev_entry,   &c->ev_side_end,  &c->ev_copied[0],  &c->ev_copied[1],
-                       &c->ev_done[0], &c->ev_done[1],   &c->ev_fork[0],    &c->ev_fork[1],
-                       &c->ev_aux_done[0], &c->ev_aux_done[1], &c->ev_aux_end};
+  hipEvent_t* evs[] = {&c->ev_entry, &c->ev_side_end, &c->ev_copied[0], &c->ev_copied[1], &c->ev_done[0],
+                       &c->ev_done[1]};
   for (hipEvent_t* ev : evs)
     if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  if (RA_BWD_TWO_STREAMS) {  // the backward's dQ stream and its fork/join events
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
+    hipEvent_t* aux_evs[] = {&c->ev_fork[0], &c->ev_fork[1], &c->ev_aux_done[0], &c->ev_aux_done[1], &c->ev_aux_end};
+    for (hipEvent_t* ev : aux_evs)
+      if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  }
   if (e != hipSuccess) {
     delete c;
     return fail(RA_ERR_HIP, "creating side stream/events: %s", hipGetErrorString(e));
