@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-clock", action="store_true",
                    help="skip the rocm-smi shader-clock sample (for runs under a profiler)")
-    p.add_argument("--cpu-rows", type=int, default=128, help="query rows in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=192, help="query rows in the CPU oracle sample")
     p.add_argument("--copy-ref-mib", type=int, default=0,
                    help="before timing, run one plain device copy of this many MiB (a reference kernel of "
                         "known traffic for scaling profiler byte counters)")
@@ -129,24 +129,23 @@ def cpu_baseline(w, rows: int):
 
 
 def cpu_baseline_decode(w, threads: int):
-    """The fp64 decode oracle on the K/V heads' first query heads (every row, the whole context)."""
+    """The fp64 decode oracle on the whole decode workload (every query head and row, the whole context)."""
     import numpy as np
 
     import oracle
     from workloads import gen_block
     c, group = w.block_len, w.heads // w.kv_heads
-    heads = [g * group for g in range(min(4, w.kv_heads))]
-    kvh = [h // group for h in heads]
-    k = [gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype)[:, kvh] for j in range(w.n_blocks)]
-    v = [gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype)[:, kvh] for j in range(w.n_blocks)]
-    q = gen_block(w.seed, "q", 0, w.q_len, w.heads, w.head_dim, w.dtype)[:, heads]
+    heads = list(range(w.heads))
+    k = [gen_block(w.seed, "k", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(w.n_blocks)]
+    v = [gen_block(w.seed, "v", j, c, w.kv_heads, w.head_dim, w.dtype) for j in range(w.n_blocks)]
+    q = gen_block(w.seed, "q", 0, w.q_len, w.heads, w.head_dim, w.dtype)
     t0 = time.time()
     oracle.decode_forward(q, k, v, w.seq_len)
     dt = time.time() - t0
     flop = 4.0 * w.head_dim * len(heads) * w.q_len * w.seq_len
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 numpy decode oracle, {w.q_len} query rows x {len(heads)} heads "
-                       f"(one per K/V head) against all {w.seq_len} keys ({dt:.1f}s)"),
+            "sample": (f"fp64 numpy decode oracle, the whole workload: {w.q_len} query rows x {len(heads)} heads "
+                       f"against all {w.seq_len} keys ({dt:.1f}s)"),
             "seconds": dt}
 
 
@@ -346,13 +345,13 @@ def run_ffn(args, w, torch, ra):
             threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
         except Exception:  # pragma: no cover
             threads = os.cpu_count() or 1
-        sel = np.linspace(0, w.rows - 1, 4096).astype(np.int64)
+        sel = np.arange(w.rows)  # the whole block (about 10 s of fp64 work on 16 cores)
         t0 = time.time()
         oracle.ffn_forward(x[sel], w1, b1, w2, b2)
         dt = time.time() - t0
         result["cpu_baseline"] = {"value": 4.0 * len(sel) * w.hidden * w.ffn / dt / 1e12, "unit": "TFLOP/s",
                                   "cores": int(threads), "kind": "oracle",
-                                  "sample": f"fp64 numpy feedforward oracle on {len(sel)} of the {w.rows} rows "
+                                  "sample": f"fp64 numpy feedforward oracle on all {len(sel)} rows of the block "
                                             f"({dt:.1f}s)", "seconds": dt}
     else:
         result["cpu_baseline"] = None
