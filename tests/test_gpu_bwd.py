@@ -28,6 +28,8 @@ CASES = [
     # |dV| at 7.4 on key 0, where bf16 rounding of P alone -- emulated in fp64 -- already
     # costs 1.36e-2, the kernel's exact error; GQA 2 keeps that floor at 7.5e-3.)
     ("bf16", 64, 4, 2, 96, 3, True),
+    ("bf16", 128, 16, 1, 96, 2, False),   # group 16: more query heads per K/V head than waves
+    ("bf16", 128, 2, 2, 300, 2, True),    # several tiles: diagonal band and ragged tail in one block
 ]
 
 
