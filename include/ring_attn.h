@@ -251,8 +251,12 @@ int ring_attn_profile_read(double* ms, int* count, double* copy_ms, double* hidd
  *   k_blocks   host array[n_blocks] of device bf16 [block_len][kv_heads][head_dim];
  *   v_blocks   key t of block j sits at global position j * block_len + t
  *   n_blocks   1 .. 64;  block_len >= 1;  q_len >= 1;  q_pos0 >= 0
- *   heads, kv_heads  heads % kv_heads == 0 and (heads / kv_heads) * q_len <= 32
- *              (RA_ERR_UNSUPPORTED otherwise);  head_dim in {64, 128}
+ *   heads, kv_heads  heads % kv_heads == 0 and heads / kv_heads <= 32
+ *              (RA_ERR_UNSUPPORTED otherwise);  head_dim in {64, 128}.  One pass
+ *              serves at most 32 query rows per K/V head ((heads / kv_heads) x
+ *              rows); a longer q_len runs as successive passes of
+ *              floor(32 / (heads / kv_heads)) rows, each of which streams the K/V
+ *              blocks again
  *   out        device, fp32 [q_len][heads][head_dim], overwritten
  *   lse        device, fp32 [heads][q_len] (natural log), overwritten
  * A key is visible to a query iff its position is <= the query's (q_pos0 >=

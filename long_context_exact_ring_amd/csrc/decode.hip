@@ -12,8 +12,9 @@
 // Kernel 1 (decode_partial_kernel): one wavefront per (K/V block, K/V head,
 // key chunk).  The wave streams its chunk through a private double-buffered
 // LDS region (LDS DMA, no barriers: a wave only reads what it copied) and
-// keeps the rows of its K/V head's query group -- group * q_len <= 32 rows,
-// one per lane of the 32x32 MFMA accumulator -- with the same transposed
+// keeps the rows of its K/V head's query group -- group * q_len <= 32 rows in
+// one launch (the host runs a longer query block as several such passes), one
+// per lane of the 32x32 MFMA accumulator -- with the same transposed
 // score / online-softmax / P-fed-back layout as the forward step.  It writes
 // a normalised partial (o, lse) per row.
 // Kernel 2 (decode_merge_kernel): one workgroup per (K/V head, row) folds the
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   __syncthreads();
   if (mx == kNegInf) {  // no visible key for this row (uniform over the workgroup)
     for (int d = tid; d < D; d += 256) orow[d] = 0.f;
-    if (tid == 0) a.lse[(size_t)head * a.q_len + qi] = kNegInf;
+    if (tid == 0) a.lse[(size_t)head * (a.ls ? a.ls : a.q_len) + qi] = kNegInf;
     return;
   }
   float z = 0.f;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   for (int u = 0; u < D / 64; ++u) red[w][lane + 64 * u] = acc[u];
   __syncthreads();
   for (int d = tid; d < D; d += 256) orow[d] = red[0][d] + red[1][d] + red[2][d] + red[3][d];
-  if (tid == 0) a.lse[(size_t)head * a.q_len + qi] = lse;
+  if (tid == 0) a.lse[(size_t)head * (a.ls ? a.ls : a.q_len) + qi] = lse;
 }
 
 static bool decode_args_ok(const DecodeArgs& a) {

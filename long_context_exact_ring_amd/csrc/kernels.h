@@ -94,13 +94,14 @@ struct DecodeArgs {
   const void* kblk[kDecodeMaxBlocks];   // block j: [len][hkv][D] bf16
   const void* vblk[kDecodeMaxBlocks];
   float* out;                           // [q_len][hq][D]
-  float* lse;                           // [hq][q_len]
+  float* lse;                           // [hq][ls] (this call's rows 0..q_len-1 of each head's row)
   float* part_o;
   float* part_lse;
   long long q_pos0;                     // global position of query row 0
   int n_blocks, len, q_len, hq, hkv, group;
   int chunk, n_chunks, n_parts;         // keys per wave, chunks per block, partials per row
   float scale_log2;
+  int ls = 0;                           // elements between heads in lse (0: q_len)
 };
 hipError_t launch_decode_partial(const DecodeArgs& a, int head_dim, hipStream_t st);
 

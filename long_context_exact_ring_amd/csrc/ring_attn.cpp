@@ -758,9 +758,11 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   if (head_dim != 64 && head_dim != 128)
     return fail(RA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
   const int group = heads / kv_heads;
-  if ((long long)group * q_len > 32)
-    return fail(RA_ERR_UNSUPPORTED, "decode takes at most 32 query rows per K/V head (group %d x q_len %d)", group,
-                q_len);
+  if (group > 32)
+    return fail(RA_ERR_UNSUPPORTED, "decode takes at most 32 query heads per K/V head (group %d)", group);
+  // a pass holds at most 32 query rows per K/V head (group x rows of the pass); longer
+  // query blocks run as successive passes over row chunks, each streaming the K/V again
+  const int pass_rows = std::min(q_len, 32 / group);
   if (q_pos0 < 0) return fail(RA_ERR_INVALID_ARG, "q_pos0 must be >= 0");
   if ((double)block_len * kv_heads * head_dim >= 2147483647.0)
     return fail(RA_ERR_INVALID_ARG, "block_len*kv_heads*head_dim exceeds 2^31-1");
@@ -783,7 +785,7 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   const double target = std::max(256.0, std::min(8192.0, total / (double)RA_DEC_WAVES));
   const int chunk = 1 << (int)std::lround(std::log2(target));
   const int n_chunks = (block_len + chunk - 1) / chunk;
-  const int rows = group * q_len;
+  const int rows = group * pass_rows;
   const size_t n_parts = (size_t)n_blocks * n_chunks;
   const size_t need = (size_t)kv_heads * n_parts * rows * (head_dim + 1) * sizeof(float);
 
@@ -813,14 +815,22 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   a.n_chunks = n_chunks;
   a.n_parts = (int)n_parts;
   a.scale_log2 = 1.4426950408889634f * rsqrt_dim(head_dim);
+  a.ls = q_len;
   ++g_prof_call;
-  {
-    ProfScope ps(KIND_DEC_PART, stream);
-    RA_HIP(launch_decode_partial(a, head_dim, stream));
-  }
-  {
-    ProfScope ps(KIND_DEC_MERGE, stream);
-    RA_HIP(launch_decode_merge(a, head_dim, stream));
+  for (int r0 = 0; r0 < q_len; r0 += pass_rows) {  // the passes share the partials buffer in stream order
+    a.q = static_cast<const char*>(q) + (size_t)r0 * heads * head_dim * 2;
+    a.out = out + (size_t)r0 * heads * head_dim;
+    a.lse = lse + r0;
+    a.q_pos0 = q_pos0 + r0;
+    a.q_len = std::min(pass_rows, q_len - r0);
+    {
+      ProfScope ps(KIND_DEC_PART, stream);
+      RA_HIP(launch_decode_partial(a, head_dim, stream));
+    }
+    {
+      ProfScope ps(KIND_DEC_MERGE, stream);
+      RA_HIP(launch_decode_merge(a, head_dim, stream));
+    }
   }
   return RA_OK;
 }

@@ -170,7 +170,7 @@ def test_decode_validation_before_any_hip_call():
     assert call(ql=0) == ra.RA_ERR_INVALID_ARG
     assert call(hq=6, hkv=4) == ra.RA_ERR_INVALID_ARG
     assert call(d=96) == ra.RA_ERR_UNSUPPORTED
-    assert call(ql=9) == ra.RA_ERR_UNSUPPORTED          # group 4 x 9 rows > 32
+    assert call(hq=66, hkv=2) == ra.RA_ERR_UNSUPPORTED  # group 33: more than 32 rows even for one query
     assert call(pos=-1) == ra.RA_ERR_INVALID_ARG
     assert call(l=o + 16) == ra.RA_ERR_INVALID_ARG       # lse inside out
     assert call(o=kb[1]) == ra.RA_ERR_INVALID_ARG        # out overlaps a K block

@@ -26,6 +26,8 @@ CASES = [
     (128, 16, 1, 256, 1, 2, "end"),    # group 16 x 2 rows = 32, a ring of one
     (64, 2, 2, 5000, 2, 1, 7777),      # long blocks, cut inside block 1
     (128, 8, 2, 64, 64, 2, 3000),      # the most blocks one call takes (64), cut inside block 46
+    (128, 32, 8, 700, 3, 20, "end"),   # group 4 x 20 rows: passes of 8, 8 and 4 rows
+    (64, 8, 1, 300, 2, 9, 250),        # group 8 x 9 rows: passes of 4, 4, 1; causal cut in block 0
 ]
 
 
