@@ -244,3 +244,33 @@ def test_binding_refuses_strided_views():
     kb = [torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")]
     with pytest.raises(ValueError, match="contiguous"):
         ra.fwd(q.transpose(0, 1), kb, kb, causal=False, rank=0)
+
+
+def test_shutdown_then_reuse_gives_identical_results():
+    """ring_attn_shutdown releases every per-device stream, event and buffer; the next
+    calls rebuild them lazily and must reproduce the earlier results bit for bit."""
+    require_gpu()
+    dtype, d, h, c, D = "bf16", 128, 2, 256, 3
+    q, k, v = _inputs(53, dtype, d, h, h, c, D)
+    do = gen_small(53, (c * D, h, d), dtype, 1.0, 3)
+    kb = [dev(k[j * c:(j + 1) * c], dtype) for j in range(D)]
+    vb = [dev(v[j * c:(j + 1) * c], dtype) for j in range(D)]
+    qd, dod = dev(q[2 * c:3 * c], dtype), dev(do[2 * c:3 * c], dtype)
+    x = dev(gen_small(53, (256, 128), dtype, 1.0, 4), dtype)
+    w1 = dev(gen_small(53, (512, 128), dtype, 0.09, 5), dtype)
+    w2 = dev(gen_small(53, (128, 512), dtype, 0.045, 6), dtype)
+
+    def run():
+        o, l = ra.fwd(qd, kb, vb, causal=True, rank=2)
+        dkb = [torch.zeros((c, h, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+        dvb = [torch.zeros((c, h, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+        g, _, _ = ra.bwd(qd, kb, vb, o, dod, l, causal=True, rank=2, dk_blocks=dkb, dv_blocks=dvb)
+        y = ra.ffn_blockwise(x, w1, w2, chunk_rows=128)
+        torch.cuda.synchronize()
+        return [o, l, g, y] + dkb + dvb
+
+    first = run()
+    ra.ring_attn_shutdown()
+    second = run()
+    for i, (a, b) in enumerate(zip(first, second)):
+        assert torch.equal(a, b), f"output {i} changed after shutdown"
