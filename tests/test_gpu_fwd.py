@@ -274,3 +274,27 @@ def test_shutdown_then_reuse_gives_identical_results():
     second = run()
     for i, (a, b) in enumerate(zip(first, second)):
         assert torch.equal(a, b), f"output {i} changed after shutdown"
+
+
+def test_calls_order_against_the_callers_stream():
+    """K/V blocks written on a (delayed) caller stream right before the call are what the
+    ring reads: the rotation copies on the library's side stream wait for the work
+    already enqueued on the caller's stream."""
+    require_gpu()
+    dtype, d, h, c, D = "bf16", 128, 2, 512, 4
+    q, k, v = _inputs(59, dtype, d, h, h, c, D)
+    kb = [dev(k[j * c:(j + 1) * c], dtype) for j in range(D)]
+    vb = [dev(v[j * c:(j + 1) * c], dtype) for j in range(D)]
+    qd = dev(q[c:2 * c], dtype)
+    o_ref, l_ref = ra.fwd(qd, kb, vb, causal=False, rank=1)
+    kb2 = [torch.zeros_like(x) for x in kb]
+    vb2 = [torch.zeros_like(x) for x in vb]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(20_000_000)  # a bounded spin keeps the caller's stream busy for a few ms
+        for dst, src in zip(kb2 + vb2, kb + vb):
+            dst.copy_(src)
+        o, l = ra.fwd(qd, kb2, vb2, causal=False, rank=1)
+    s.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
