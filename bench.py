@@ -551,6 +551,8 @@ def main():
         sys.exit(2)
     import torch
 
+    from long_context_exact_ring_amd.build import build_if_missing
+    build_if_missing()  # loads what is built; builds only in a fresh checkout
     import long_context_exact_ring_amd as ra
     from workloads import FFN_WORKLOADS, WORKLOADS
 

@@ -11,3 +11,6 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+    # a fresh checkout has no library yet: build it once (hipcc cross-compiles without a GPU)
+    from long_context_exact_ring_amd.build import build_if_missing
+    build_if_missing(verbose=False)
