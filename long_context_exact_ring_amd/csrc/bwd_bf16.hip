@@ -291,346 +291,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_pair_kernel(ArgPair<Bwd
   dkdv_body<D, BR, NW, KLDS, LAG>(a);
 }
 
-// ============================================== dK / dV, one wave per SIMD
-// The same gradients as dkdv_body with one wave of 32 keys per SIMD, so each
-// wave owns the SIMD's whole register file: V stays in registers as a B
-// operand (the workgroup's K rows are staged in LDS once), dK/dV accumulate in
-// the accumulation registers, and two sets of S/dP accumulators fit beside
-// them.  With no
-// second wave to fill the matrix core while the exponentials run, the wave is
-// software-pipelined by one query tile and scheduled by hand:
-//   iteration t:  [S, dP of tile t+1]  x  [P, dS of tile t, two scores per MFMA pair]
-//                 [dV, dK of tile t]   x  [LDS reads for the next iteration]
-// Every LDS read is issued two MFMA pairs before its use, and sched_barrier
-// fences keep the compiler from regrouping the slots.  Four LDS stages with
-// the tile DMA three tiles ahead: after the barrier of iteration t, tiles up
-// to t+2 are in LDS, so the reads that start iteration t+1 can be issued at the
-// end of iteration t.
-template <int D, int NW>
-__device__ __forceinline__ void dkdv1_body(const BwdArgs& a) {
-  constexpr int BR = 32;
-  constexpr int ROWB = D * 2;
-  constexpr int TILEB = BR * ROWB;
-  constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
-  constexpr int NB = 4;
-  constexpr int NK = D / 16;  // k slices of S and dP (one MFMA pair each)
-  constexpr int NT = D / 32;  // 32-wide column tiles of dK and dV
-  constexpr int EPS = 16 / NK;  // scores of tile t formed per S/dP MFMA pair
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NB * STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ktile[NW * 32 * ROWB];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  const int KW = NW * 32;
-  const int nkt = (a.len + KW - 1) / KW;
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int kt = logical % nkt;  // ascending: with a causal diagonal, low key tiles are heaviest
-  const int g = logical / nkt;
-  const int kb0 = kt * KW;
-  const int key0 = kb0 + wu * 32;
-  const int key = key0 + n;
-  const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
-
-  using BF = Frag<bf16_storage>;
-  BF vf[NK];
-  {
-    const int kr = min(key, a.len - 1);  // lanes past the end compute garbage that is never stored
-    const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) vf[ks] = frag_load<bf16_storage>(vp + ks * 16);
-  }
-  // the workgroup's K rows (rows past the end re-read the last row)
-  dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len, ktile,
-                           wu, lane);
-
-  f32x16_t dkT[NT], dvT[NT];
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt) {
-    dkT[dt] = f32x16_t{};
-    dvT[dt] = f32x16_t{};
-  }
-
-  const int nqt = (a.len + BR - 1) / BR;
-  const int qt_lo = a.diag ? kb0 / BR : 0;  // earlier tiles precede every key
-  const int per_head = nqt - qt_lo;
-  const int iters = per_head * a.group;
-  if (iters <= 0) return;  // uniform over the workgroup
-
-  // Tile DMA.  A full tile is this wave's IPW 1 KB instructions per operand,
-  // at fixed per-lane byte offsets from a scalar per-tile base; a ragged last
-  // tile takes the row-clamped path.
-  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16;  // rows and 16-byte chunks per instruction
-  constexpr int IPW = BR / RPI / NW;
-  static_assert((BR / RPI) % NW == 0, "tile DMA must split evenly over the waves");
-  uint32_t toff[IPW];
-#pragma unroll
-  for (int j = 0; j < IPW; ++j) {
-    const int r = (wu * IPW + j) * RPI + lane / CPR, slot = lane % CPR;
-    toff[j] = (uint32_t)((size_t)r * qstride * 2 + (size_t)((slot ^ swz<D>(r)) * 16));
-  }
-  auto issue = [&](int it, unsigned char* st) {
-    const int hh = it / per_head, qt = qt_lo + it % per_head;
-    const int head = g * a.group + hh;
-    const int r0 = qt * BR;
-    if (r0 + BR <= a.len) {
-      const size_t base = ((size_t)r0 * qstride + (size_t)head * D) * 2;
-      const unsigned char* qsrc = reinterpret_cast<const unsigned char*>(a.q) + base;
-      const unsigned char* dsrc = reinterpret_cast<const unsigned char*>(a.dout) + base;
-#pragma unroll
-      for (int j = 0; j < IPW; ++j) {
-        const uint32_t dst = (uint32_t)(wu * IPW + j) * 1024;
-        lds_dma16_off(qsrc, toff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + dst)));
-        lds_dma16_off(dsrc, toff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + TILEB + dst)));
-      }
-    } else {
-      dma_rows<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.q) + (size_t)head * D, qstride, r0, a.len, st, wu,
-                          lane);
-      dma_rows<D, BR, NW>(reinterpret_cast<const bf16_storage*>(a.dout) + (size_t)head * D, qstride, r0, a.len,
-                          st + TILEB, wu, lane);
-    }
-    if (wu == NW - 1) {  // row terms [lse2(BR) | Delta(BR)]: 64 dwords, the last wave
-      const int r = min(r0 + (lane % BR), a.len - 1);
-      const float* src = (lane < BR ? a.lse2 : a.delta) + (size_t)head * a.ls + r;
-      lds_dma4(src, __builtin_amdgcn_readfirstlane(lds_addr(st + 2 * TILEB)));
-    }
-  };
-
-  const LdsOperandOffsets<D> lo(lane, 0);
-  auto ld_row = [&](const unsigned char* tile, int ks) {  // B/A operand with k = D, row n
-    return BF{*reinterpret_cast<const uint4*>(tile + lo.k[ks])};
-  };
-  const unsigned char* kw = ktile + wu * 32 * ROWB;  // this wave's K rows (same swizzle as rows 0..31)
-  auto ld_tr = [&](const unsigned char* tile, int dt, int kc) {  // transposed 32-column operand
-    const uint2 v0 = ds_read_tr16(tile + kc * 16 * ROWB + lo.v[dt][0]);
-    const uint2 v1 = ds_read_tr16(tile + kc * 16 * ROWB + lo.v[dt][1]);
-    return BF{make_uint4(v0.x, v0.y, v1.x, v1.y)};
-  };
-  // Row terms of CNT consecutive scores from i0 (i0 % CNT == 0): rows
-  // crow(i, hf), i.e. CNT consecutive rows from 8*(i0/4) + 4*hf + i0%4.
-  const uint32_t rto = hf * 16;
-  auto ld_terms = [&](const unsigned char* st, int i0, auto cnt_tag) {
-    constexpr int CNT = decltype(cnt_tag)::value;
-    const unsigned char* pl = st + 2 * TILEB + rto + ((i0 >> 2) * 8 + (i0 & 3)) * 4;
-    struct {
-      float l[CNT], d[CNT];
-    } t;
-    if constexpr (CNT == 1) {
-      t.l[0] = *reinterpret_cast<const float*>(pl);
-      t.d[0] = *reinterpret_cast<const float*>(pl + BR * 4);
-    } else if constexpr (CNT == 2) {
-      const float2 l2 = *reinterpret_cast<const float2*>(pl), d2 = *reinterpret_cast<const float2*>(pl + BR * 4);
-      t.l[0] = l2.x, t.l[1] = l2.y, t.d[0] = d2.x, t.d[1] = d2.y;
-    } else {
-      static_assert(CNT == 4, "one, two or four scores per slot");
-      const float4 l4 = *reinterpret_cast<const float4*>(pl), d4 = *reinterpret_cast<const float4*>(pl + BR * 4);
-      t.l[0] = l4.x, t.l[1] = l4.y, t.l[2] = l4.z, t.l[3] = l4.w;
-      t.d[0] = d4.x, t.d[1] = d4.y, t.d[2] = d4.z, t.d[3] = d4.w;
-    }
-    return t;
-  };
-  auto pack = [](float x, float y) {
-    const f32x2_t v = {x, y};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-  };
-
-  // Scores 0..7 (P/dS fragment 0) are formed in the NK slots of phase 1, EP1
-  // per slot; scores 8..15 (fragment 1) in the NT phase-2 slots that consume
-  // fragment 0, EP2 per slot.
-  constexpr int EP1 = 8 / NK, EP2 = 8 / NT;
-  constexpr int TRD = 3;  // transposed operands are read TRD slots ahead
-  using T1 = std::integral_constant<int, EP1>;
-  using T2 = std::integral_constant<int, EP2>;
-  using Terms1 = decltype(ld_terms(smem, 0, T1{}));
-  using Terms2 = decltype(ld_terms(smem, 0, T2{}));
-
-  // carried between iterations: S/dP of the current tile (two sets, by parity),
-  // and the operands of the next iteration's first two slots (Q, dO and K k
-  // slices of tile it+2's S/dP, row terms of tile it+1)
-  f32x16_t sA, dpA, sB, dpB;
-  BF qn[2], dn[2], kn[2];
-  Terms1 tn[2];
-
-  // iteration `it`, whose tile sits in stage S
-  auto iteration = [&](auto stage_tag, int it, f32x16_t& s_cur, f32x16_t& dp_cur, f32x16_t& s_nxt,
-                       f32x16_t& dp_nxt) {
-    constexpr int S = decltype(stage_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of tile it+2 has landed
-    __syncthreads();  // ... everyone's; every wave is past tile it-1, so its stage is free
-    if (it + 3 < iters) issue(it + 3, smem + ((S + 3) % NB) * STAGE);
-    const unsigned char* cur = smem + S * STAGE;
-    const unsigned char* nx1 = smem + ((S + 1) % NB) * STAGE;  // tile it+1 (garbage past the end: unused)
-    const unsigned char* nx2 = smem + ((S + 2) % NB) * STAGE;
-    // The mask is applied to every tile (two compares and a select per score,
-    // in the shadow of the matrix core): one code path keeps the register
-    // allocation the hand schedule relies on.  Score i sits in row
-    // r0 + crow(i, hf) = r0 + 4*hf + c_i with c_i a constant; it is kept iff
-    // lo_c <= c_i < hi_c (rows below the lane's key on the diagonal see no
-    // key, rows past the end do not exist).
-    const int r0 = (qt_lo + it % per_head) * BR;
-    const int lo_c = (a.diag ? key : 0) - r0 - 4 * hf;
-    const int hi_c = a.len - r0 - 4 * hf;
-    float pv_[16], dsv_[16];
-    uint32_t pw[8], sw[8];
-    auto score = [&](int i, float l, float d) {
-      float pv = fast_exp2(__builtin_fmaf(s_cur[i], a.scale_log2, -l));
-      const int ci = crow(i, 0);  // a constant once unrolled
-      pv = (ci >= lo_c && ci < hi_c) ? pv : 0.f;
-      pv_[i] = pv;
-      dsv_[i] = pv * (dp_cur[i] - d);
-      if (i & 1) {
-        pw[i >> 1] = pack(pv_[i - 1], pv_[i]);
-        sw[i >> 1] = pack(dsv_[i - 1], dsv_[i]);
-      }
-    };
-
-    // phase 1: S, dP of tile it+1; scores 0..7 of tile it
-    BF qb[NK], db[NK], kb[NK];
-    Terms1 tb[NK];
-    Terms2 tc[NT];
-    qb[0] = qn[0], qb[1] = qn[1];
-    db[0] = dn[0], db[1] = dn[1];
-    kb[0] = kn[0], kb[1] = kn[1];
-    tb[0] = tn[0], tb[1] = tn[1];
-    BF trd[2 * NT], trq[2 * NT];
-    s_nxt = f32x16_t{};
-    dp_nxt = f32x16_t{};
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (k + 2 < NK) {
-        qb[k + 2] = ld_row(nx1, k + 2);
-        db[k + 2] = ld_row(nx1 + TILEB, k + 2);
-        kb[k + 2] = ld_row(kw, k + 2);
-        tb[k + 2] = ld_terms(cur, (k + 2) * EP1, T1{});
-      }
-      if (k >= NK - 2) tc[k - (NK - 2)] = ld_terms(cur, 8 + (k - (NK - 2)) * EP2, T2{});
-      if (k >= NK - TRD) {  // the first transposed operands of phase 2
-        const int m = k - (NK - TRD);
-        trd[m] = ld_tr(cur + TILEB, m % NT, m / NT);
-        trq[m] = ld_tr(cur, m % NT, m / NT);
-      }
-      mma(s_nxt, qb[k], kb[k]);
-      mma(dp_nxt, db[k], vf[k]);
-#pragma unroll
-      for (int u = 0; u < EP1; ++u) score(k * EP1 + u, tb[k].l[u], tb[k].d[u]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const BF pf0{make_uint4(pw[0], pw[1], pw[2], pw[3])}, sf0{make_uint4(sw[0], sw[1], sw[2], sw[3])};
-
-    // phase 2: dV, dK of tile it (scores 8..15 formed while fragment 0 is
-    // consumed); the reads that start the next iteration
-    BF pf1, sf1;
-#pragma unroll
-    for (int m = 0; m < 2 * NT; ++m) {
-      const int c2 = m / NT, dt = m % NT;
-      if (m + TRD < 2 * NT) {
-        trd[m + TRD] = ld_tr(cur + TILEB, (m + TRD) % NT, (m + TRD) / NT);
-        trq[m + TRD] = ld_tr(cur, (m + TRD) % NT, (m + TRD) / NT);
-      }
-      if (m + 2 < NT) tc[m + 2] = ld_terms(cur, 8 + (m + 2) * EP2, T2{});
-      if (m == 2 * NT - 2) {
-        qn[0] = ld_row(nx2, 0);
-        dn[0] = ld_row(nx2 + TILEB, 0);
-        kn[0] = ld_row(kw, 0);
-        tn[0] = ld_terms(nx1, 0, T1{});
-      }
-      if (m == 2 * NT - 1) {
-        qn[1] = ld_row(nx2, 1);
-        dn[1] = ld_row(nx2 + TILEB, 1);
-        kn[1] = ld_row(kw, 1);
-        tn[1] = ld_terms(nx1, EP1, T1{});
-      }
-      if (c2 == 0) {
-        mma(dvT[dt], trd[m], pf0);
-        mma(dkT[dt], trq[m], sf0);
-#pragma unroll
-        for (int u = 0; u < EP2; ++u) score(8 + m * EP2 + u, tc[m].l[u], tc[m].d[u]);
-        if (m == NT - 1) {
-          pf1 = BF{make_uint4(pw[4], pw[5], pw[6], pw[7])};
-          sf1 = BF{make_uint4(sw[4], sw[5], sw[6], sw[7])};
-        }
-      } else {
-        mma(dvT[dt], trd[m], pf1);
-        mma(dkT[dt], trq[m], sf1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto step = [&](auto stage_tag, int it) {
-    if constexpr ((decltype(stage_tag)::value & 1) == 0)
-      iteration(stage_tag, it, sA, dpA, sB, dpB);
-    else
-      iteration(stage_tag, it, sB, dpB, sA, dpA);
-  };
-
-  // prologue: K rows and tiles 0..2 in flight, S/dP of tile 0, the reads that start iteration 0
-  issue(0, smem);
-  if (iters > 1) issue(1, smem + STAGE);
-  if (iters > 2) issue(2, smem + 2 * STAGE);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  sA = f32x16_t{};
-  dpA = f32x16_t{};
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    mma(sA, ld_row(smem, ks), ld_row(kw, ks));
-    mma(dpA, ld_row(smem + TILEB, ks), vf[ks]);
-  }
-  tn[0] = ld_terms(smem, 0, T1{});
-  tn[1] = ld_terms(smem, EP1, T1{});
-  qn[0] = ld_row(smem + STAGE, 0);
-  qn[1] = ld_row(smem + STAGE, 1);
-  dn[0] = ld_row(smem + STAGE + TILEB, 0);
-  dn[1] = ld_row(smem + STAGE + TILEB, 1);
-  kn[0] = ld_row(kw, 0);
-  kn[1] = ld_row(kw, 1);
-
-  int it = 0;
-  for (; it + NB <= iters; it += NB) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
-    step(std::integral_constant<int, 2>{}, it + 2);
-    step(std::integral_constant<int, 3>{}, it + 3);
-  }
-  if (it < iters) step(std::integral_constant<int, 0>{}, it);
-  if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
-  if (it + 2 < iters) step(std::integral_constant<int, 2>{}, it + 2);
-
-  if (key >= a.len) return;
-  float* dkp = a.dk + (size_t)key * kvstride + (size_t)g * D;
-  float* dvp = a.dv + (size_t)key * kvstride + (size_t)g * D;
-#pragma unroll
-  for (int dt = 0; dt < NT; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = dt * 32 + j * 8 + hf * 4;
-      float4* pk = reinterpret_cast<float4*>(dkp + d0);
-      float4* pv = reinterpret_cast<float4*>(dvp + d0);
-      float4 ok = *pk, ov = *pv;
-      ok.x += a.scale * dkT[dt][4 * j];
-      ok.y += a.scale * dkT[dt][4 * j + 1];
-      ok.z += a.scale * dkT[dt][4 * j + 2];
-      ok.w += a.scale * dkT[dt][4 * j + 3];
-      ov.x += dvT[dt][4 * j];
-      ov.y += dvT[dt][4 * j + 1];
-      ov.z += dvT[dt][4 * j + 2];
-      ov.w += dvT[dt][4 * j + 3];
-      *pk = ok;
-      *pv = ov;
-    }
-}
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv1_bf16_kernel(BwdArgs a) {
-  dkdv1_body<D, NW>(a);
-}
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv1_bf16_pair_kernel(ArgPair<BwdArgs> pair) {
-  const BwdArgs a = pair.s[blockIdx.y];
-  dkdv1_body<D, NW>(a);
-}
-
 // =================================================================== dQ
 template <int D, int BC, int NW>
 __device__ __forceinline__ void dq_body(const BwdArgs& a) {
@@ -813,32 +473,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_pair_kernel(ArgPair<BwdAr
 #define RA_BWD_BC 64  // dQ kernel: keys per tile (64 measured 5% faster than 32)
 #endif
 
-#ifndef RA_KV_ONEWAVE
-// 1: dK/dV with one wave of 32 keys per SIMD (dkdv1_body).  Off: parity
-// holds, but the lone wave is instruction-issue bound (6.4 VALU instructions
-// per MFMA, matrix core busy 0.40 against 0.52) and runs 15% slower than
-// dkdv_body on a 8192 x 8192, 32-head block pair.
-#define RA_KV_ONEWAVE 0
-#endif
-constexpr int kKv1NW = 4;
-
-template <int D>
-static hipError_t launch_dkdv1_bf16_t(const BwdArgs* a, int nsub, hipStream_t st) {
-  const int KW = kKv1NW * 32;
-  const int nblk = ((a[0].len + KW - 1) / KW) * a[0].hkv;
-  if (nblk == 0) return hipSuccess;
-  ArgPair<BwdArgs> pair{};
-  for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];
-  if (nsub == 1)
-    hipLaunchKernelGGL((bwd_dkdv1_bf16_kernel<D, kKv1NW>), dim3(nblk), dim3(kKv1NW * 64), 0, st, a[0]);
-  else
-    hipLaunchKernelGGL((bwd_dkdv1_bf16_pair_kernel<D, kKv1NW>), dim3(nblk, nsub), dim3(kKv1NW * 64), 0, st, pair);
-  return hipGetLastError();
-}
-
 template <int D>
 static hipError_t launch_dkdv_bf16_t(const BwdArgs* a, int nsub, hipStream_t st) {
-  if (RA_KV_ONEWAVE) return launch_dkdv1_bf16_t<D>(a, nsub, st);
   const int KW = kKvNW * 32;
   const int nblk = ((a[0].len + KW - 1) / KW) * a[0].hkv;
   if (nblk == 0) return hipSuccess;

@@ -150,186 +150,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void gemm_bt_kernel(GemmArgs a) {
   }
 }
 
-// One wave per SIMD, 128x128 per wave (16 accumulator tiles in the
-// accumulation registers), four waves for a 256x256 workgroup tile, k-steps of
-// 64 through two LDS stages.  The k-step's four 16-wide slices are issued by
-// hand: the fragments of slice kk+1 are read while the 16 MFMAs of slice kk
-// run, and the workgroup barrier sits inside the last slice, after its
-// fragments have arrived, so the next k-step's first reads and the DMA of the
-// k-step after it overlap the last MFMAs.
-template <bool GELU_BF16_OUT>
-__global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
-  constexpr int TM = 4, TN = 4, WGM = 2, WGN = 2, NW = 4;
-  constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;  // 256 x 256
-  constexpr int ROWB = kGemmBK * 2;                      // 128 bytes per tile row
-  constexpr int ATILE = BM * ROWB, BTILE = BN * ROWB;
-  constexpr int STAGE = ATILE + BTILE;
-  constexpr int NKK = kGemmBK / 16;  // k slices per k-step
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int n = lane & 31, hf = lane >> 5;
-  const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wu % WGM, wn = wu / WGM;
-
-  const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ntn = a.n / BN, ntm = (a.m + BM - 1) / BM;
-  const int band = logical / (a.group * ntn), first_m = band * a.group;
-  const int gm = min(ntm - first_m, a.group), in_band = logical - band * a.group * ntn;
-  const int tm = first_m + in_band % gm, tn = in_band / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // DMA lane offsets: a 1 KB instruction moves 8 rows of 128 bytes
-  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16;
-  constexpr int IPA = BM / RPI / NW, IPB = BN / RPI / NW;  // 8 + 8 per wave
-  uint32_t aoff[IPA], boff[IPB];
-#pragma unroll
-  for (int j = 0; j < IPA; ++j) {
-    const int r = (wu * IPA + j) * RPI + lane / CPR, slot = lane % CPR;
-    const int mr = min(m0 + r, a.m - 1);  // rows past the end re-read the last row (never stored)
-    aoff[j] = (uint32_t)(((size_t)mr * a.lda + (slot ^ swz<64>(r)) * 8) * 2);
-  }
-#pragma unroll
-  for (int j = 0; j < IPB; ++j) {
-    const int r = (wu * IPB + j) * RPI + lane / CPR, slot = lane % CPR;
-    boff[j] = (uint32_t)(((size_t)(n0 + r) * a.ldb + (slot ^ swz<64>(r)) * 8) * 2);
-  }
-  const unsigned char* abase = reinterpret_cast<const unsigned char*>(a.a);
-  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(a.b);
-  // DMA instruction d (0..IPA+IPB-1) of k-step ks into stage st (A rows first)
-  auto issue1 = [&](int ks, unsigned char* st, int d) {
-    const size_t kb = (size_t)ks * kGemmBK * 2;
-    if (d < IPA)
-      lds_dma16_off(abase + kb, aoff[d], __builtin_amdgcn_readfirstlane(lds_addr(st + (uint32_t)(wu * IPA + d) * 1024)));
-    else
-      lds_dma16_off(bbase + kb, boff[d - IPA],
-                    __builtin_amdgcn_readfirstlane(lds_addr(st + ATILE + (uint32_t)(wu * IPB + d - IPA) * 1024)));
-  };
-  constexpr int ND = IPA + IPB, NDA = 6;  // DMA instructions per k-step; issued right after the barrier
-
-  // LDS read offsets: rows 32 apart share a swizzle, so one offset per k slice
-  // serves all four fragments of an operand (the rest are immediates)
-  uint32_t xo[NKK], wo[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int ra = wm * TM * 32 + n, rb = wn * TN * 32 + n;
-    xo[kk] = (uint32_t)(ra * ROWB + (((kk * 2 + hf) ^ swz<64>(ra)) * 16));
-    wo[kk] = (uint32_t)(ATILE + rb * ROWB + (((kk * 2 + hf) ^ swz<64>(rb)) * 16));
-  }
-  using BF = Frag<bf16_storage>;
-  auto rd = [&](const unsigned char* st, uint32_t off, int t) {
-    return BF{*reinterpret_cast<const uint4*>(st + off + t * 32 * ROWB)};
-  };
-
-  f32x16_t acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = f32x16_t{};
-
-  const int nk = a.k / kGemmBK;
-  // The DMA of k-step ks+2 starts after the barrier inside step ks (NDA
-  // instructions) and finishes in the first slices of step ks+1, one
-  // instruction per MFMA pair, so no burst of loads stalls the MFMAs behind it.
-  // Targets past the end re-read the last k-step (harmless, never used).
-#pragma unroll
-  for (int d = 0; d < ND; ++d) issue1(0, smem, d);
-#pragma unroll
-  for (int d = 0; d < NDA; ++d) issue1(min(1, nk - 1), smem + STAGE, d);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  BF wf[TN], xf[TM];  // fragments of the slice being multiplied
-#pragma unroll
-  for (int t = 0; t < TN; ++t) wf[t] = rd(smem, wo[0], t);
-#pragma unroll
-  for (int t = 0; t < TM; ++t) xf[t] = rd(smem, xo[0], t);
-
-  // k-step ks in stage S; on entry wf/xf hold slice 0 of ks
-  auto kstep = [&](auto stage_tag, int ks) {
-    constexpr int S = decltype(stage_tag)::value;
-    const unsigned char* st = smem + S * STAGE;
-    const unsigned char* nx = smem + (S ^ 1) * STAGE;
-    const int kc = min(ks + 1, nk - 1), k2 = min(ks + 2, nk - 1);  // DMA targets
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      BF wn_[TN], xn_[TM];
-      const bool last = kk == NKK - 1;
-#pragma unroll
-      for (int q = 0; q < TN * TM; ++q) {
-        const int i = q / TM, j = q % TM;
-        if (!last) {  // the next slice's fragments, one read per MFMA pair
-          if (q % 2 == 0 && q / 2 < TN) wn_[q / 2] = rd(st, wo[kk + 1], q / 2);
-          if (q % 2 == 1 && q / 2 < TM) xn_[q / 2] = rd(st, xo[kk + 1], q / 2);
-          // the rest of k-step ks+1's DMA (into the other stage)
-          const int d = NDA + kk * (TN * TM / 2) + q / 2;
-          if (q % 2 == 1 && d < ND) issue1(kc, smem + (S ^ 1) * STAGE, d);
-        } else if (q == 4) {
-          // every fragment of this stage has been read: sync, start refilling
-          // it with k-step ks+2, and start reading k-step ks+1 from the other
-          // stage
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-        }
-        if (last && q > 4 && q % 2 == 1 && (q - 5) / 2 < NDA) issue1(k2, smem + S * STAGE, (q - 5) / 2);
-        if (last && q >= 4) {  // (past the last k-step these read stale data that is never used)
-          if (q % 2 == 0 && (q - 4) / 2 < TN) wn_[(q - 4) / 2] = rd(nx, wo[0], (q - 4) / 2);
-          if (q % 2 == 1 && (q - 4) / 2 < TM) xn_[(q - 4) / 2] = rd(nx, xo[0], (q - 4) / 2);
-        }
-        mma(acc[i][j], wf[i], xf[j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int t = 0; t < TN; ++t) wf[t] = wn_[t];
-#pragma unroll
-      for (int t = 0; t < TM; ++t) xf[t] = xn_[t];
-    }
-  };
-  int ks = 0;
-  for (; ks + 2 <= nk; ks += 2) {
-    kstep(std::integral_constant<int, 0>{}, ks);
-    kstep(std::integral_constant<int, 1>{}, ks + 1);
-  }
-  if (ks < nk) kstep(std::integral_constant<int, 0>{}, ks);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (unused) re-reads land before the workgroup ends
-
-  // epilogue: lane holds output row m = m0 + (wm*TM + j)*32 + n and columns
-  // n0 + (wn*TN + i)*32 + crow(r, hf) for the 16 accumulator registers r
-#pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int m = m0 + (wm * TM + j) * 32 + n;
-    if (m >= a.m) continue;
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = n0 + (wn * TN + i) * 32 + q4 * 8 + hf * 4;  // four consecutive columns
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = acc[i][j][4 * q4 + e];
-          if (a.bias) v[e] += a.bias[c0 + e];
-        }
-        if constexpr (GELU_BF16_OUT) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
-          f32x2_t lo = {v[0], v[1]}, hi = {v[2], v[3]};
-          const uint2 packed = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
-                                          __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_storage*>(a.c) + (size_t)m * a.ldc + c0) = packed;
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.c) + (size_t)m * a.ldc + c0) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        }
-      }
-  }
-}
-
-#ifndef RA_GEMM_ONEWAVE
-// 1: 256x256 tiles by gemm1_kernel (one wave per SIMD).  Off: parity holds,
-// but the 2048 x 16384 x 4096 up-projection takes 346 us against 298 us with
-// the eight-wave kernel; both hold one k-step of DMA ahead and stall on it.
-#define RA_GEMM_ONEWAVE 0
-#endif
-
 #ifndef RA_GEMM_BIG
 #define RA_GEMM_BIG 1  // 0: always the 128x128 tile; 1: 256-wide tiles where the shape allows
 #endif
@@ -355,17 +175,8 @@ hipError_t launch_gemm_bt(const GemmArgs& args, bool gelu_bf16_out, hipStream_t 
   GemmArgs a = args;
   a.group = a.k <= 8192 ? 4 : 8;
   // 256x256 tiles (8 waves of 64x128) when the columns allow it and the grid still fills the chip
-  if (RA_GEMM_BIG && a.n % 256 == 0 && (long)((a.m + 255) / 256) * (a.n / 256) >= 256) {
-    if (RA_GEMM_ONEWAVE) {
-      const long nblk = (long)((a.m + 255) / 256) * (a.n / 256);
-      if (gelu_bf16_out)
-        hipLaunchKernelGGL((gemm1_kernel<true>), dim3((unsigned)nblk), dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((gemm1_kernel<false>), dim3((unsigned)nblk), dim3(256), 0, st, a);
-      return hipGetLastError();
-    }
+  if (RA_GEMM_BIG && a.n % 256 == 0 && (long)((a.m + 255) / 256) * (a.n / 256) >= 256)
     return launch_gemm_cfg<2, 4, 4, 2>(a, gelu_bf16_out, st);
-  }
   // 128x256 tiles (four 64x128 waves) for shorter row blocks
   if (RA_GEMM_BIG >= 2 && a.n % 256 == 0 && (long)((a.m + 127) / 128) * (a.n / 256) >= 256)
     return launch_gemm_cfg<2, 4, 2, 2>(a, gelu_bf16_out, st);
