@@ -58,6 +58,14 @@ def parse():
                         "rocprofv3 --pmc pass of SQ counters")
     p.add_argument("--summarize-overlap", nargs=2, metavar=("KERNEL_TRACE_CSV", "MEMORY_COPY_TRACE_CSV"),
                    help="no GPU work: share of the device-to-device copy time hidden under kernels")
+    p.add_argument("--summarize-gaps", metavar="KERNEL_TRACE_CSV",
+                   help="no GPU work: idle time of the compute stream between consecutive kernels of the timed "
+                        "steps of a rocprofv3 --kernel-trace run of this bench (same --steps/--warmup), i.e. an "
+                        "upper bound on the exposed K/V rotation copy time")
+    p.add_argument("--sweep-block-len", action="store_true",
+                   help="the overlap condition of the ring: for block lengths 1024..16384 (32 heads x 128, "
+                        "non-causal, one rank against 8 blocks) measure per-round kernel time, copy time and "
+                        "the exposed copy time, next to the prediction from c_min = F/B")
     return p.parse_args()
 
 
@@ -396,7 +404,7 @@ def profiled_traffic(kind: str, head_dim: int, dtype: str, workload: str):
 COMMON_SOURCES = ("kcommon.h", "kernels.h")
 KERNEL_SOURCES = (("fwd_bf16_kernel", ("fwd_step.hip", "fwd_common.h", "tile_stage.h")),
                   ("bwd_dkdv_bf16_kernel", ("bwd_bf16.hip",)), ("bwd_dq_bf16_kernel", ("bwd_bf16.hip",)),
-                  ("bwd_pre_kernel", ("bwd_step.hip", "tile_stage.h")), ("decode_", ("decode.hip",)),
+                  ("bwd_pre_kernel", ("merge.hip",)), ("decode_", ("decode.hip",)),
                   ("gemm_bt_kernel", ("ffn.hip",)), ("merge", ("merge.hip",)))
 
 
@@ -534,6 +542,100 @@ def summarize_overlap(kernel_trace_csv: str, copy_trace_csv: str):
     return hidden / max(total, 1)
 
 
+def summarize_gaps(trace_csv: str, steps: int, warmup: int, copy_ms_per_step=None):
+    """Idle time of the compute stream inside the timed steps of a kernel-trace run.
+
+    Every kernel of a ring step runs on the caller's stream; the K/V copies run on
+    the copy engine and the stream only waits when a round's block has not arrived.
+    So the gaps between consecutive kernels (launch latency included) bound the
+    exposed copy time from above.  The bench's kernels are the same in every step:
+    the timed steps are the last steps/(warmup+steps) of the kernels before the
+    matrix-core rate probe that follows the timed region."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    first = next(i for i, n in enumerate(names) if "fwd_bf16_kernel" in n or "fwd_step_kernel" in n)
+    probe = next((i for i, n in enumerate(names) if "mfma_rate_kernel" in n), len(rows))
+    ring = rows[first:probe]
+    if len(ring) % (steps + warmup):
+        sys.exit(f"{len(ring)} kernels do not split into {steps + warmup} equal steps")
+    per = len(ring) // (steps + warmup)
+    timed = ring[-steps * per:]
+    gaps = [max(0, int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) for a, b in zip(timed, timed[1:])]
+    busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed)
+    span = int(timed[-1]["End_Timestamp"]) - int(timed[0]["Start_Timestamp"])
+    gap_ms = sum(gaps) / 1e6 / steps
+    out = {"kernels_per_step": per, "span_ms_per_step": span / 1e6 / steps, "kernel_ms_per_step": busy / 1e6 / steps,
+           "idle_ms_per_step": gap_ms, "largest_gap_us": max(gaps) / 1e3 if gaps else 0.0,
+           "gaps_over_20us": sum(1 for g in gaps if g > 20000) / steps}
+    if copy_ms_per_step:
+        out["copy_ms_per_step"] = copy_ms_per_step
+        out["hidden_frac_lower_bound"] = max(0.0, 1.0 - gap_ms / copy_ms_per_step)
+    print(json.dumps(out))
+    return out
+
+
+def sweep_block_len(args, torch, ra):
+    """Per-round compute and copy time against the block length (the overlap condition).
+
+    One rank's non-causal forward against D = 8 blocks of 32 heads x 128: every round
+    is a full c x c block pair, the K/V copy of the next round (2 c Hkv d bf16 bytes)
+    runs while the current round computes (4 d Hq c^2 flop).  The copy is hidden when
+    c >= c_min = (F / B) (Hkv / Hq), F the forward kernel's rate and B the copy
+    engine's, both measured here.  Exposed copy time per round is the call's wall time
+    minus its kernel time, over the rounds that waited for a copy."""
+    from workloads import bf16_bits, gen_block
+    D, hq, hkv, d = 8, 32, 32, 128
+    res = []
+    for c in (1024, 2048, 4096, 8192, 16384):
+        def up(x):
+            return torch.from_numpy(bf16_bits(x).view("int16")).view(torch.bfloat16).cuda()
+        kb = [up(gen_block(11, "k", j, c, hkv, d, "bf16")) for j in range(D)]
+        vb = [up(gen_block(11, "v", j, c, hkv, d, "bf16")) for j in range(D)]
+        q = up(gen_block(11, "q", 0, c, hq, d, "bf16"))
+        out = torch.empty((c, hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((hq, c), dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            ra.fwd(q, kb, vb, causal=False, rank=0, out=out, lse=lse)
+        torch.cuda.synchronize()
+        reps = max(3, min(40, int(2e4 / c)))
+        ra.ring_attn_profile_enable(True)
+        ra.ring_attn_profile_read()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ra.fwd(q, kb, vb, causal=False, rank=0, out=out, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        recs, copy_ms, _ = ra.ring_attn_profile_read()
+        ra.ring_attn_profile_enable(False)
+        wall = e0.elapsed_time(e1) / reps
+        kms, kcnt = recs["fwd_step"]
+        cms, ccnt = recs["copy"]
+        t_k, t_c = kms / kcnt, cms / ccnt                      # per round
+        F = 4.0 * d * hq * c * c / (t_k * 1e-3)                # flop/s of one full round
+        B = 2.0 * 2 * c * hkv * d / (t_c * 1e-3)               # bytes/s of one K+V copy
+        c_min = F / B * hkv / hq
+        exposed = max(0.0, wall - kms / reps)                  # per call (D - 1 copied rounds)
+        pred = (D - 1) * max(0.0, t_c - t_k)
+        res.append({"block_len": c, "kernel_ms_per_round": t_k, "copy_ms_per_round": t_c,
+                    "fwd_tflops": F / 1e12, "copy_gbs": B / 1e9, "c_min": c_min,
+                    "exposed_ms_per_call": exposed, "predicted_exposed_ms_per_call": pred,
+                    "wall_ms_per_call": wall})
+        log(f"[sweep] c={c}: kernel {t_k:.3f} ms, copy {t_c:.3f} ms per round, c_min {c_min:.0f}, "
+            f"exposed {exposed:.3f} ms (predicted {pred:.3f}) per call")
+        del kb, vb, q, out, lse
+        torch.cuda.empty_cache()
+    print("| block_len c | kernel ms / round | copy ms / round | forward TFLOP/s | copy GB/s | c_min = (F/B)(Hkv/Hq) "
+          "| exposed ms / call (measured) | exposed ms / call (predicted, (D-1) max(0, copy - kernel)) |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in res:
+        print(f"| {r['block_len']} | {r['kernel_ms_per_round']:.3f} | {r['copy_ms_per_round']:.3f} | "
+              f"{r['fwd_tflops']:.0f} | {r['copy_gbs']:.0f} | {r['c_min']:.0f} | {r['exposed_ms_per_call']:.3f} | "
+              f"{r['predicted_exposed_ms_per_call']:.3f} |")
+    print(json.dumps({"sweep": res}))
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -544,6 +646,9 @@ def main():
         return
     if args.summarize_overlap:
         summarize_overlap(*args.summarize_overlap)
+        return
+    if args.summarize_gaps:
+        summarize_gaps(args.summarize_gaps, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
@@ -556,6 +661,10 @@ def main():
     import long_context_exact_ring_amd as ra
     from workloads import FFN_WORKLOADS, WORKLOADS
 
+    if args.sweep_block_len:
+        torch.cuda.set_device(0)
+        sweep_block_len(args, torch, ra)
+        return
     if args.workload in FFN_WORKLOADS:
         torch.cuda.set_device(0)
         run_ffn(args, FFN_WORKLOADS[args.workload], torch, ra)
@@ -661,6 +770,16 @@ def main():
     overlap = {"copy_ms_per_step": copy_ms / args.steps, "hidden_ms_per_step": hidden_ms / args.steps,
                "hidden_frac": (hidden_ms / copy_ms) if copy_ms > 0 else None,
                "copy_engine": os.environ.get("RING_ATTN_COPY", "sdma")}
+    # the overlap condition c >= c_min = (F / B)(Hkv / Hq), with F the forward kernels' rate
+    # and B the copy engine's rate, both measured in this run
+    if "copy" in kern and "fwd_step" in kern:
+        copy_bytes = 2.0 * c * hkv * d * (2 if w.dtype == "bf16" else 4)  # K + V of one block
+        B = copy_bytes / (kern["copy"]["avg_launch_ms"] * 1e-3)
+        F = fwd_flop / (kern["fwd_step"]["ms_per_step"] * 1e-3)
+        elem = 2 if w.dtype == "bf16" else 4
+        overlap["copy_gbs"] = round(B / 1e9, 1)
+        overlap["c_min_tokens"] = round(F / B * hkv / hq * elem / 2, 1)
+        overlap["block_len_over_c_min"] = round(c / overlap["c_min_tokens"], 2)
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -41,8 +41,12 @@
  *  - Pointers are caller-owned device memory (no ownership transfer).  The
  *    library owns one side stream, a few events and the K/V staging buffers
  *    per device (created lazily, released by ring_attn_shutdown).
- *  - Calls that overlap in time on one device (different streams) share the
- *    staging buffers and race; serialise them on one stream.
+ *  - Calls on one device share the library's staging and workspace buffers.
+ *    Calls issued on different streams of the device are serialised on the
+ *    GPU: a call's work starts only after the previous call's work (on
+ *    whichever stream it was issued) has finished, so they never race; the
+ *    price is that they do not overlap.  ring_attn_merge uses no library
+ *    buffer and is not ordered against other calls.
  *  - Errors: every entry point returns RA_OK (0) or an ra_status code and
  *    never aborts.  Arguments are validated on the host before anything is
  *    enqueued; on a validation error nothing is enqueued and no output is
@@ -117,7 +121,10 @@ int ring_attn_merge(const float* out_a, const float* lse_a, const float* out_b,
 
 /*
  * ring_attn_bwd -- one rank's backward ring step (bf16 inputs), recomputing the
- * attention probabilities from the saved lse of the forward.
+ * attention probabilities from the saved lse of the forward.  The method is a
+ * training method: the ring runs inside every transformer layer (close-reading
+ * notes, abstract and the §3.5 algorithm), so the gradients flow through the
+ * same blockwise ring as the forward, with the same K/V rotation.
  *
  * With P = softmax of the visible scaled scores (rebuilt as exp(S - lse)),
  * Delta_i = sum_d dout_i * out_i, dS = P * (dout V^T - Delta):
@@ -128,6 +135,15 @@ int ring_attn_merge(const float* out_a, const float* lse_a, const float* out_b,
  * For grouped heads the dk/dv of a K/V head sum over its query heads.  Run
  * over every rank, the accumulated dk/dv are the full-sequence gradients; the
  * caller zeroes them once before the first rank.
+ *
+ * Precision: the kernels convert q, the K/V blocks and dout exactly to IEEE
+ * half and run every contraction on fp16 matrix cores with fp32
+ * accumulation, so the probabilities and dS they round for the matrix core
+ * keep 11 significant bits (bf16 would keep 8).  Inputs must be finite and
+ * below 65504 in magnitude (the half range), as must dS; values below 2^-14
+ * keep an absolute step of 2^-24.  The library holds, per device, a
+ * workspace of the row terms (8 bytes per query row and head) and the half
+ * copies of q, dout and one K/V block.
  *
  *   out, lse   the forward's fp32 outputs for this rank
  *   dout       device, bf16 [block_len][heads][head_dim]
@@ -197,9 +213,13 @@ int ring_attn_debug(int poison, long long delay_cycles);
 const char* ring_attn_last_error(void);
 
 /*
- * Bytes of library-owned staging for a block shape: two K and two V blocks
- * (the block in use by the kernel is either the rank's own or a staged one;
- * the in-flight block goes to the other half).  elem_bytes is 2 (bf16) or 4.
+ * Bytes of library-owned staging for a block shape: two K and two V blocks.
+ * This is the resident-block budget of the close-reading notes, §3.4: besides
+ * Q and the output, a host holds the K/V block in use and the K/V block in
+ * flight from the previous host (the block in use by the kernel is either the
+ * rank's own or a staged one; the in-flight block goes to the other half).
+ * elem_bytes is 2 (bf16) or 4.  Returns 0 for non-positive sizes or an
+ * elem_bytes other than 2 or 4.
  */
 size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int elem_bytes);
 
@@ -212,8 +232,7 @@ size_t ring_attn_workspace_bytes(int block_len, int kv_heads, int head_dim, int 
  * RA_ERR_INVALID_ARG and enqueue nothing.  (NULL, 0) returns to library-owned
  * staging.  The call synchronises the device first, so no earlier call still
  * uses the old buffer, and frees the library's own buffer if it had one.
- * The backward's row-term buffer (8 bytes per query row and head) stays
- * library-owned.  Errors: RA_ERR_INVALID_ARG (pointer/size mismatch,
+ * The backward's workspace (row terms and half copies) stays library-owned.  Errors: RA_ERR_INVALID_ARG (pointer/size mismatch,
  * misalignment), RA_ERR_HIP.
  */
 int ring_attn_set_workspace(void* dev_ptr, size_t bytes);

@@ -249,10 +249,47 @@ def ring_attn_shutdown() -> None:
 
 
 # ------------------------------------------------------------------ tensor conveniences
-def _dims(q, k0) -> Tuple[int, int, int, int]:
+# The conveniences check, on the host and before anything is enqueued, that every
+# tensor has exactly the shape, dtype and device the C call will read or write:
+# the library only sees raw pointers, so a short or mistyped buffer would be read
+# or written past its end on the GPU.
+def _expect(t, name: str, shape: Tuple[int, ...], dtype, device) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+
+
+def _expect_blocks(ts: Sequence, name: str, n: int, shape, dtype, device) -> None:
+    if len(ts) != n:
+        raise ValueError(f"{name}: expected {n} blocks, got {len(ts)}")
+    for j, t in enumerate(ts):
+        _expect(t, f"{name}[{j}]", shape, dtype, device)
+
+
+def _dims(q, k_blocks) -> Tuple[int, int, int, int]:
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [block_len, heads, head_dim], got shape {tuple(q.shape)}")
+    if len(k_blocks) < 1:
+        raise ValueError("k_blocks: at least one block is needed")
+    if k_blocks[0].dim() != 3:
+        raise ValueError(f"k_blocks[0]: expected [block_len, kv_heads, head_dim], got shape {tuple(k_blocks[0].shape)}")
     block_len, heads, head_dim = q.shape
-    kv_heads = k0.shape[1]
+    kv_heads = k_blocks[0].shape[1]
     return block_len, heads, kv_heads, head_dim
+
+
+def _check_ring_inputs(q, k_blocks, v_blocks):
+    """Shared checks of fwd/bwd: q [c, Hq, d]; every K/V block [c, Hkv, d] of q's dtype and device."""
+    import torch
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    c, hq, hkv, d = _dims(q, k_blocks)
+    _expect_blocks(k_blocks, "k_blocks", len(k_blocks), (c, hkv, d), q.dtype, q.device)
+    _expect_blocks(v_blocks, "v_blocks", len(k_blocks), (c, hkv, d), q.dtype, q.device)
+    return c, hq, hkv, d
 
 
 def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None, lse=None, stream=None,
@@ -261,14 +298,14 @@ def fwd(q, k_blocks: List, v_blocks: List, *, causal: bool, rank: int, out=None,
 
     zigzag=True selects the load-balanced layout (block b holds chunks b and 2D-1-b; bf16 only)."""
     import torch
-    c, hq, hkv, d = _dims(q, k_blocks[0])
+    c, hq, hkv, d = _check_ring_inputs(q, k_blocks, v_blocks)
     if out is None:
         out = torch.empty((c, hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((hq, c), dtype=torch.float32, device=q.device)
+    _expect(out, "out", (c, hq, d), torch.float32, q.device)
+    _expect(lse, "lse", (hq, c), torch.float32, q.device)
     fn = ring_attn_fwd if q.dtype == torch.bfloat16 else ring_attn_fwd_f32
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError(f"unsupported dtype {q.dtype}")
     if zigzag:
         if q.dtype != torch.bfloat16:
             raise TypeError("the zig-zag layout takes bf16 inputs")
@@ -281,13 +318,19 @@ def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank
         dk_blocks=None, dv_blocks=None, stream=None, zigzag: bool = False):
     """Backward ring step; dk/dv blocks are accumulated into (zero-initialised if not given)."""
     import torch
-    c, hq, hkv, d = _dims(q, k_blocks[0])
+    c, hq, hkv, d = _check_ring_inputs(q, k_blocks, v_blocks)
+    _expect(out, "out", (c, hq, d), torch.float32, q.device)
+    _expect(dout, "dout", (c, hq, d), q.dtype, q.device)
+    _expect(lse, "lse", (hq, c), torch.float32, q.device)
     if dq is None:
         dq = torch.empty((c, hq, d), dtype=torch.float32, device=q.device)
     if dk_blocks is None:
         dk_blocks = [torch.zeros((c, hkv, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
     if dv_blocks is None:
         dv_blocks = [torch.zeros((c, hkv, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
+    _expect(dq, "dq", (c, hq, d), torch.float32, q.device)
+    _expect_blocks(dk_blocks, "dk_blocks", len(k_blocks), (c, hkv, d), torch.float32, q.device)
+    _expect_blocks(dv_blocks, "dv_blocks", len(k_blocks), (c, hkv, d), torch.float32, q.device)
     fn = ring_attn_bwd if q.dtype == torch.bfloat16 else ring_attn_bwd_f32
     if zigzag:
         if q.dtype != torch.bfloat16:
@@ -301,12 +344,21 @@ def bwd(q, k_blocks: List, v_blocks: List, out, dout, lse, *, causal: bool, rank
 def decode(q, k_blocks: List, v_blocks: List, *, q_pos0: int, out=None, lse=None, stream=None):
     """Decode step: q [q_len, Hq, d] bf16 against every block; returns (out, lse)."""
     import torch
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [q_len, heads, head_dim], got shape {tuple(q.shape)}")
+    _expect(q, "q", tuple(q.shape), torch.bfloat16, q.device)
     q_len, hq, d = q.shape
+    if len(k_blocks) < 1 or k_blocks[0].dim() != 3:
+        raise ValueError("k_blocks: expected at least one [block_len, kv_heads, head_dim] block")
     block_len, hkv = k_blocks[0].shape[0], k_blocks[0].shape[1]
+    _expect_blocks(k_blocks, "k_blocks", len(k_blocks), (block_len, hkv, d), torch.bfloat16, q.device)
+    _expect_blocks(v_blocks, "v_blocks", len(k_blocks), (block_len, hkv, d), torch.bfloat16, q.device)
     if out is None:
         out = torch.empty((q_len, hq, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((hq, q_len), dtype=torch.float32, device=q.device)
+    _expect(out, "out", (q_len, hq, d), torch.float32, q.device)
+    _expect(lse, "lse", (hq, q_len), torch.float32, q.device)
     _check(ring_attn_decode(q, k_blocks, v_blocks, len(k_blocks), block_len, q_len, hq, hkv, d, q_pos0, out, lse,
                             stream))
     return out, lse
@@ -315,20 +367,39 @@ def decode(q, k_blocks: List, v_blocks: List, *, q_pos0: int, out=None, lse=None
 def ffn_blockwise(x, w1, w2, *, b1=None, b2=None, chunk_rows: int = 0, y=None, stream=None):
     """y = GELU(x W1^T + b1) W2^T + b2 over row chunks; x [rows, hidden] bf16, weights [out, in] bf16."""
     import torch
+    if x.dim() != 2 or w1.dim() != 2:
+        raise ValueError("x and w1 must be 2-D ([rows, hidden] and [ffn, hidden])")
     rows, hidden = x.shape
     ffn = w1.shape[0]
+    _expect(x, "x", (rows, hidden), torch.bfloat16, x.device)
+    _expect(w1, "w1", (ffn, hidden), torch.bfloat16, x.device)
+    _expect(w2, "w2", (hidden, ffn), torch.bfloat16, x.device)
+    if b1 is not None:
+        _expect(b1, "b1", (ffn,), torch.float32, x.device)
+    if b2 is not None:
+        _expect(b2, "b2", (hidden,), torch.float32, x.device)
     if y is None:
         y = torch.empty((rows, hidden), dtype=torch.float32, device=x.device)
+    _expect(y, "y", (rows, hidden), torch.float32, x.device)
     _check(ring_attn_ffn_blockwise(x, w1, b1, w2, b2, rows, hidden, ffn, chunk_rows, y, stream))
     return y
 
 
 def merge(out_a, lse_a, out_b, lse_b, *, out=None, lse=None, stream=None):
     import torch
+    if out_a.dim() != 3:
+        raise ValueError(f"out_a: expected [rows, heads, head_dim], got shape {tuple(out_a.shape)}")
     rows, heads, head_dim = out_a.shape
+    dev = out_a.device
+    _expect(out_a, "out_a", (rows, heads, head_dim), torch.float32, dev)
+    _expect(out_b, "out_b", (rows, heads, head_dim), torch.float32, dev)
+    _expect(lse_a, "lse_a", (heads, rows), torch.float32, dev)
+    _expect(lse_b, "lse_b", (heads, rows), torch.float32, dev)
     if out is None:
         out = torch.empty_like(out_a)
     if lse is None:
         lse = torch.empty_like(lse_a)
+    _expect(out, "out", (rows, heads, head_dim), torch.float32, dev)
+    _expect(lse, "lse", (heads, rows), torch.float32, dev)
     _check(ring_attn_merge(out_a, lse_a, out_b, lse_b, rows, heads, head_dim, out, lse, stream))
     return out, lse

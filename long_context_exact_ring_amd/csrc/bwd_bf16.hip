@@ -8,6 +8,16 @@
 // Attention with Blockwise Transformers for Near-Infinite Context", §3.5 --
 // so the same rotated K/V blocks drive the backward.)
 //
+// Operand precision: the inputs are bf16, but every contraction here runs on
+// fp16 MFMA.  Q and dO reach these kernels as half copies made by the
+// preprocess kernel, the dK/dV kernel converts its K and V rows when it loads
+// them (and writes the half K/V rows out for the dQ kernel of the same round).
+// The conversion is exact for the inputs' values, so S and dP are the same
+// products as in bf16; what changes is the rounding of P and dS, the operands
+// the kernels produce themselves: 11 significant bits instead of 8, an eighth
+// of the error in dV, dK and dQ.  Inputs must stay below 65504 in magnitude
+// (the half range); below 2^-14 a half keeps an absolute step of 2^-24.
+//
 // Same building blocks as the bf16 forward: streamed tiles are copied
 // global -> LDS by LDS DMA into unpadded, XOR-swizzled rows; operands whose
 // contraction index runs along the tile rows are read with transposed LDS
@@ -15,7 +25,7 @@
 // tiles run in separate (masked) loops so the hot loop carries no masking.
 //
 //  * dK/dV kernel: a wave owns 32 keys (B operands with keys on lanes: V in
-//    registers, the workgroup's K rows staged in LDS once) and walks the query
+//    registers, the wave's K rows written to LDS once) and walks the query
 //    tiles of every query head of its group, two tiles per barrier.  S and dP
 //    come out with keys on lanes, so P and dS are B operands of
 //    dV^T += dO^T P and dK^T += Q^T dS, whose A operands are transposed reads
@@ -39,31 +49,21 @@ namespace {
 #ifndef RA_KV_NW
 #define RA_KV_NW 8
 #endif
-#ifndef RA_KV_KLDS
-#define RA_KV_KLDS 1
-#endif
-#ifndef RA_KV_LAG
-#define RA_KV_LAG 0  // 1: second wave per SIMD half a tile behind (+1% alone, -1% with RA_KV_PAIR)
-#endif
-#ifndef RA_KV_PAIR
-#define RA_KV_PAIR 1  // one barrier per two query tiles (+1.7% on dK/dV)
-#endif
 constexpr int kBwdNW = RA_BWD_NW;  // dQ kernel: waves per workgroup (2 per SIMD)
 constexpr int kKvNW = RA_KV_NW;    // dK/dV kernel: waves per workgroup (2 per SIMD; K rows read from LDS)
 
 }  // namespace
 
 // =================================================================== dK / dV
-template <int D, int BR, int NW, bool KLDS, bool LAG>
+template <int D, int BR, int NW>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   constexpr int ROWB = D * 2;
   constexpr int TILEB = BR * ROWB;
   constexpr int STAGE = 2 * TILEB + 2 * BR * 4;  // Q tile, dO tile, lse2[BR], Delta[BR]
-  // LDS stages.  PAIR: one barrier per two query tiles, the DMA of the next
-  // two tiles issued right after it (two more stages).
-  constexpr bool PAIR = RA_KV_PAIR != 0;
-  constexpr int NB = (LAG ? 3 : 2) + (PAIR ? 2 : 0);
-  constexpr int KTB = KLDS ? NW * 32 * ROWB : 16;  // the workgroup's K rows (KLDS: read from LDS)
+  // Four LDS stages: one barrier per two query tiles, the DMA of the next two
+  // tiles issued right after it.
+  constexpr int NB = 4;
+  constexpr int KTB = NW * 32 * ROWB;  // the workgroup's K rows (half), read from LDS
   static_assert(BR % 32 == 0 && (BR == 32 || BR % 64 == 0), "row-term DMA covers 64 dwords per wave");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NB * STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char ktile[KTB];
@@ -82,24 +82,40 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const int key = key0 + n;
   const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
 
-  Frag<bf16_storage> kf[KLDS ? 1 : D / 16], vf[D / 16];
+  // K and V become half operands here.  The workgroup's K rows are copied to
+  // LDS by DMA (each wave moves exactly its own 32 rows), converted in place by
+  // that wave, and written back out as halves with whole-row stores; this
+  // lane's V row is loaded and converted in registers (B operands with keys
+  // on lanes) and written out too.  The half copies feed the dQ kernel of the
+  // same round: every key of every K/V head belongs to exactly one workgroup.
+  dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
+                           ktile, wu, lane);
+  Frag<bf16_storage> vf[D / 16];
   {
     const int kr = min(key, a.len - 1);  // lanes past the end compute garbage that is never stored
-    const bf16_storage* kp = reinterpret_cast<const bf16_storage*>(a.k) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
-    const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + (size_t)kr * kvstride + (size_t)g * D + hf * 8;
+    const size_t off = (size_t)kr * kvstride + (size_t)g * D + hf * 8;
+    const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + off;
+    bf16_storage* v16 = reinterpret_cast<bf16_storage*>(a.v16) + off;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      if constexpr (!KLDS) kf[ks] = frag_load<bf16_storage>(kp + ks * 16);
-      vf[ks] = frag_load<bf16_storage>(vp + ks * 16);
+    for (int ks = 0; ks < D / 16; ++ks) vf[ks].v = bf16x8_to_f16x8(ld16(vp + ks * 16));
+    if (key < a.len)
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) st16(v16 + ks * 16, vf[ks].v);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's K rows have landed
+  {
+    constexpr int CPR = ROWB / 16, RPI = 64 / CPR;  // 16-byte chunks per row, rows per pass
+    bf16_storage* k16 = reinterpret_cast<bf16_storage*>(a.k16) + (size_t)g * D;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = wu * 32 + i * RPI + lane / CPR, slot = lane % CPR;
+      uint4* p = reinterpret_cast<uint4*>(ktile + r * ROWB + slot * 16);
+      const uint4 kh = bf16x8_to_f16x8(*p);
+      *p = kh;
+      if (kb0 + r < a.len) st16(k16 + (size_t)(kb0 + r) * kvstride + ((slot ^ swz<D>(r)) * 8), kh);
     }
   }
-  if constexpr (KLDS) {  // the workgroup's K rows go to LDS once; waves read their 32 rows as B operands
-    dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
-                             ktile, wu, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // settle the K/V loads before the pipelined loop
+  __syncthreads();  // the half K rows are in LDS
 
   f32x16_t dkT[D / 32], dvT[D / 32];
 #pragma unroll
@@ -115,6 +131,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const int per_head = nqt - qt_lo;
   const int iters = per_head * a.group;
 
+  // a.q / a.dout hold the half copies of the query block and its output gradient
   auto issue = [&](int it, unsigned char* st) {
     const int hh = it / per_head, qt = qt_lo + it % per_head;
     const int head = g * a.group + hh;
@@ -134,7 +151,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     }
   };
 
-  // part12: S = Q K^T and dP = dO V^T of one query tile, then P and dS as bf16
+  // part12: S = Q K^T and dP = dO V^T of one query tile, then P and dS as half
   // B fragments; false if every row of the tile precedes this wave's keys.
   // part3: dV^T += dO^T P and dK^T += Q^T dS with the tile's Q/dO read transposed.
   using BF = Frag<bf16_storage>;
@@ -152,11 +169,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        if constexpr (KLDS)
-          mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), row_frag<D>(ktile, wu * 32 + n, ks, hf));
-        else
-          mma(s, row_frag<D>(qn, qs * 32 + n, ks, hf), kf[ks]);
-        mma(dp, row_frag<D>(dn, qs * 32 + n, ks, hf), vf[ks]);
+        mma_h(s, row_frag<D>(qn, qs * 32 + n, ks, hf), row_frag<D>(ktile, wu * 32 + n, ks, hf));
+        mma_h(dp, row_frag<D>(dn, qs * 32 + n, ks, hf), vf[ks]);
       }
       float p[16];
 #pragma unroll
@@ -181,8 +195,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         float ds8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ds8[e] = dp[c2 * 8 + e];
-        pf[qs][c2] = frag_from_f32<bf16_storage>(p + c2 * 8);
-        sf[qs][c2] = frag_from_f32<bf16_storage>(ds8);
+        pf[qs][c2] = frag_h_from_f32(p + c2 * 8);
+        sf[qs][c2] = frag_h_from_f32(ds8);
       }
     }
     return true;
@@ -197,63 +211,33 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
         const int kc = qs * 2 + c2;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) {
-          mma(dvT[dt], tr_frag<D>(dn, dt * 32, kc, lane), pf[qs][c2]);
-          mma(dkT[dt], tr_frag<D>(qn, dt * 32, kc, lane), sf[qs][c2]);
+          mma_h(dvT[dt], tr_frag<D>(dn, dt * 32, kc, lane), pf[qs][c2]);
+          mma_h(dkT[dt], tr_frag<D>(qn, dt * 32, kc, lane), sf[qs][c2]);
         }
       }
   };
 
-  // With LAG, the second half of the waves (the second wave on every SIMD)
-  // runs half a tile behind: in the interval of tile it it first finishes
-  // tile it-1 (part3) and then starts tile it (part12), while the first half
-  // runs part12 then part3 of tile it.  The two waves sharing a SIMD are then
-  // in different phases (matrix core vs exponentials) between barriers.  Tile
-  // it-1 must stay in LDS for that interval, hence three stages.
-  // The whole tile loop is instantiated once per role, so the two programs
-  // do not share (and inflate) one register allocation.
-  auto run = [&](auto lag_tag) {
-    constexpr bool LAGGED = decltype(lag_tag)::value;
-    bool prev_active = false;
-    BF pfl[BR / 32][2], sfl[BR / 32][2];
-    int cur = 0;  // stage of tile it
-    auto step = [&](int it, auto masked_tag) {
-      const int nxt = cur + 1 == NB ? 0 : cur + 1;
-      if (!PAIR || (it & 1) == 0) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile `it` (PAIR: and it+1) has landed
-        __syncthreads();  // ... everyone's; every wave is past tile it-1, so the stages of tiles <= it-NB+1 are free
-        if constexpr (PAIR) {
-          if (it + 2 < iters) issue(it + 2, smem + (it + 2) % NB * STAGE);
-          if (it + 3 < iters) issue(it + 3, smem + (it + 3) % NB * STAGE);
-        } else {
-          if (it + 1 < iters) issue(it + 1, smem + nxt * STAGE);
-        }
-      }
-      const unsigned char* st = smem + cur * STAGE;
-      if constexpr (LAGGED) {
-        if (prev_active) part3(smem + (cur == 0 ? NB - 1 : cur - 1) * STAGE, pfl, sfl);
-        prev_active = part12(it, st, masked_tag, pfl, sfl);
-      } else {
-        BF pf[BR / 32][2], sf[BR / 32][2];
-        if (part12(it, st, masked_tag, pf, sf)) part3(st, pf, sf);
-      }
-      cur = nxt;
-    };
-    if (iters > 0) issue(0, smem);
-    if (PAIR && iters > 1) issue(1, smem + STAGE);
-    int it = 0;
-    for (int hh = 0; hh < a.group; ++hh) {
-      const int base = hh * per_head - qt_lo;  // it = base + qt
-      for (; it < base + qt_nb; ++it) step(it, std::true_type{});
-      for (; it < base + qt_full; ++it) step(it, std::false_type{});
-      for (; it < base + nqt; ++it) step(it, std::true_type{});
+  int cur = 0;  // stage of tile it
+  auto step = [&](int it, auto masked_tag) {
+    if ((it & 1) == 0) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tiles it and it+1 has landed
+      __syncthreads();  // ... everyone's; every wave is past tile it-1, so the stages of tiles it-2, it-1 are free
+      if (it + 2 < iters) issue(it + 2, smem + (it + 2) % NB * STAGE);
+      if (it + 3 < iters) issue(it + 3, smem + (it + 3) % NB * STAGE);
     }
-    if constexpr (LAGGED)
-      if (prev_active) part3(smem + (cur == 0 ? NB - 1 : cur - 1) * STAGE, pfl, sfl);
+    BF pf[BR / 32][2], sf[BR / 32][2];
+    if (part12(it, smem + cur * STAGE, masked_tag, pf, sf)) part3(smem + cur * STAGE, pf, sf);
+    cur = cur + 1 == NB ? 0 : cur + 1;
   };
-  if (LAG && wu >= NW / 2)
-    run(std::integral_constant<bool, LAG>{});
-  else
-    run(std::false_type{});
+  if (iters > 0) issue(0, smem);
+  if (iters > 1) issue(1, smem + STAGE);
+  int it = 0;
+  for (int hh = 0; hh < a.group; ++hh) {
+    const int base = hh * per_head - qt_lo;  // it = base + qt
+    for (; it < base + qt_nb; ++it) step(it, std::true_type{});
+    for (; it < base + qt_full; ++it) step(it, std::false_type{});
+    for (; it < base + nqt; ++it) step(it, std::true_type{});
+  }
 
   if (key >= a.len) return;
   float* dkp = a.dk + (size_t)key * kvstride + (size_t)g * D;
@@ -279,16 +263,16 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     }
 }
 
-template <int D, int BR, int NW, bool KLDS, bool LAG>
+template <int D, int BR, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_kernel(BwdArgs a) {
-  dkdv_body<D, BR, NW, KLDS, LAG>(a);
+  dkdv_body<D, BR, NW>(a);
 }
 // Two independent dK/dV sub-problems of one launch (blockIdx.y selects), e.g. the
 // zig-zag layout's two key chunks of a block against the same query chunk.
-template <int D, int BR, int NW, bool KLDS, bool LAG>
+template <int D, int BR, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_bf16_pair_kernel(ArgPair<BwdArgs> pair) {
   const BwdArgs a = pair.s[blockIdx.y];
-  dkdv_body<D, BR, NW, KLDS, LAG>(a);
+  dkdv_body<D, BR, NW>(a);
 }
 
 // =================================================================== dQ
@@ -385,8 +369,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
       for (int ks = 0; ks < D / 16; ++ks) {
         const Frag<bf16_storage> kf{*reinterpret_cast<const uint4*>(st + kt * 32 * ROWB + lo.k[ks])};
         const Frag<bf16_storage> vf{*reinterpret_cast<const uint4*>(st + TILEB + kt * 32 * ROWB + lo.k[ks])};
-        mma(s[kt], kf, qf[ks]);
-        mma(dp[kt], vf, of[ks]);
+        mma_h(s[kt], kf, qf[ks]);
+        mma_h(dp[kt], vf, of[ks]);
       }
     }
     const int lim = (a.diag ? min(qi, a.len - 1) : a.len - 1) - t0;  // visible local keys: <= lim
@@ -405,12 +389,12 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
       float ds8[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) ds8[e] = dp[kc >> 1][(kc & 1) * 8 + e];
-      const Frag<bf16_storage> sf = frag_from_f32<bf16_storage>(ds8);
+      const Frag<bf16_storage> sf = frag_h_from_f32(ds8);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const uint2 v0 = ds_read_tr16(st + kc * 16 * ROWB + lo.v[dt][0]);
         const uint2 v1 = ds_read_tr16(st + kc * 16 * ROWB + lo.v[dt][1]);
-        mma(dqT[dt], Frag<bf16_storage>{make_uint4(v0.x, v0.y, v1.x, v1.y)}, sf);
+        mma_h(dqT[dt], Frag<bf16_storage>{make_uint4(v0.x, v0.y, v1.x, v1.y)}, sf);
       }
     }
   };
@@ -481,11 +465,10 @@ static hipError_t launch_dkdv_bf16_t(const BwdArgs* a, int nsub, hipStream_t st)
   ArgPair<BwdArgs> pair{};
   for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];
   if (nsub == 1)
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>), dim3(nblk),
-                       dim3(kKvNW * 64), 0, st, a[0]);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, RA_BWD_BR, kKvNW>), dim3(nblk), dim3(kKvNW * 64), 0, st, a[0]);
   else
-    hipLaunchKernelGGL((bwd_dkdv_bf16_pair_kernel<D, RA_BWD_BR, kKvNW, RA_KV_KLDS != 0, RA_KV_LAG != 0>),
-                       dim3(nblk, nsub), dim3(kKvNW * 64), 0, st, pair);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_pair_kernel<D, RA_BWD_BR, kKvNW>), dim3(nblk, nsub), dim3(kKvNW * 64), 0, st,
+                       pair);
   return hipGetLastError();
 }
 

@@ -331,12 +331,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a) {
 #ifndef RA_KV_WAVES
 #define RA_KV_WAVES 8
 #endif
-#ifndef RA_DQ_BC
-#define RA_DQ_BC 64
-#endif
-#ifndef RA_KV_BR
-#define RA_KV_BR 32
-#endif
 constexpr int kBwdWaves = RA_DQ_WAVES;
 constexpr int kKvWaves = RA_KV_WAVES;
 
@@ -371,30 +365,20 @@ static bool same_bwd_grid(const BwdArgs* a, int nsub) {
 hipError_t launch_bwd_dkdv(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
   if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
   if (elem_bytes == 2) return launch_bwd_dkdv_bf16(ap, nsub, head_dim, st);
-  if (nsub != 1) return hipErrorInvalidValue;  // the fp32 path runs one sub-problem per launch
+  if (nsub != 1 || elem_bytes != 4) return hipErrorInvalidValue;  // fp32: one sub-problem per launch
   const BwdArgs& a = ap[0];
-  if (elem_bytes == 2) {
-    if (head_dim == 64) return launch_dkdv_t<bf16_storage, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dkdv_t<bf16_storage, 128, RA_KV_BR>(a, st);
-  } else {
-    if (head_dim == 64) return launch_dkdv_t<float, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dkdv_t<float, 128, 32>(a, st);
-  }
+  if (head_dim == 64) return launch_dkdv_t<float, 64, 32>(a, st);
+  if (head_dim == 128) return launch_dkdv_t<float, 128, 32>(a, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
   if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
   if (elem_bytes == 2) return launch_bwd_dq_bf16(ap, nsub, head_dim, st);
-  if (nsub != 1) return hipErrorInvalidValue;
+  if (nsub != 1 || elem_bytes != 4) return hipErrorInvalidValue;
   const BwdArgs& a = ap[0];
-  if (elem_bytes == 2) {
-    if (head_dim == 64) return launch_dq_t<bf16_storage, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dq_t<bf16_storage, 128, RA_DQ_BC>(a, st);
-  } else {
-    if (head_dim == 64) return launch_dq_t<float, 64, 32>(a, st);
-    if (head_dim == 128) return launch_dq_t<float, 128, 32>(a, st);
-  }
+  if (head_dim == 64) return launch_dq_t<float, 64, 32>(a, st);
+  if (head_dim == 128) return launch_dq_t<float, 128, 32>(a, st);
   return hipErrorInvalidValue;
 }
 

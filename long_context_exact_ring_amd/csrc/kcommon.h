@@ -71,6 +71,42 @@ template <> __device__ __forceinline__ Frag<float> frag_from_f32(const float* x)
   return Frag<float>{make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7])};
 }
 
+// fp16 operands.  The bf16 backward converts its inputs to IEEE half once
+// (exact: a bf16 value has 8 significant bits, a half 11, and every bf16 of
+// magnitude in [2^-14, 65504] is a normal half) and then runs its contractions
+// on fp16 MFMA, so the probabilities and dS it rounds for the matrix core keep
+// 11 bits instead of 8.  Half fragments travel in the same 16-byte Frag
+// storage as bf16 ones.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// c += A * B over one 16-wide k slice, both fragments holding IEEE half bits
+__device__ __forceinline__ void mma_h(f32x16_t& c, const Frag<bf16_storage>& a, const Frag<bf16_storage>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a.v), __builtin_bit_cast(f16x8_t, b.v), c,
+                                             0, 0, 0);
+}
+
+// 8 fp32 values -> half fragment (round to nearest even, v_cvt_pk_f16_f32)
+__device__ __forceinline__ Frag<bf16_storage> frag_h_from_f32(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2_t a = {x[2 * j], x[2 * j + 1]};
+    f16x2_t b = __builtin_convertvector(a, f16x2_t);
+    w[j] = __builtin_bit_cast(uint32_t, b);
+  }
+  return Frag<bf16_storage>{make_uint4(w[0], w[1], w[2], w[3])};
+}
+
+// Two bf16 values (one 32-bit word) -> two halves, in place.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  f32x2_t a = {__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(a, f16x2_t));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+  return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+
 // c += A * B over one 16-wide k slice
 __device__ __forceinline__ void mma(f32x16_t& c, const Frag<bf16_storage>& a,
                                     const Frag<bf16_storage>& b) {
@@ -121,29 +157,22 @@ __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4
 // LDS bytes the copy writes and stalls every later LDS read until the copy
 // completes, which serialises the prefetch of the next tile against the reads
 // of the current one.  The asm has no register outputs; callers make the data
-// visible with `s_waitcnt vmcnt(0)` followed by a workgroup barrier.
+// visible with `s_waitcnt vmcnt(0)` followed by a workgroup barrier.  The LDS
+// base goes in through the M0 register as an operand ("{m0}"), so the compiler
+// writes M0 itself and knows what it holds; the asm never modifies it.
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gaddr), "{m0}"(lds_base) : "memory");
 }
 
 // Same, with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset
 // (no per-lane address arithmetic when only the base moves).
 __device__ __forceinline__ void lds_dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
 // Same, 4 bytes per lane (lane i's dword lands at lds_base + 4*i).
 __device__ __forceinline__ void lds_dma4(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dword %0, off" : : "v"(gaddr), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -33,7 +33,8 @@ hipError_t launch_fwd_step(const FwdArgs* a, int nsub, int elem_bytes, int head_
 // waves per forward workgroup for an element size (the host packs heads by it)
 int fwd_waves_per_block(int elem_bytes);
 
-// Backward: Delta = rowsum(dout * out) per (head, row).
+// Backward: Delta = rowsum(dout * out) per (head, row); for bf16 inputs also
+// the half (IEEE fp16) copies of q and dout that the bf16 backward contracts.
 struct BwdPreArgs {
   const void* dout;  // [len][hq][D] bf16 or fp32
   const float* out;  // [len][hq][D]
@@ -42,15 +43,22 @@ struct BwdPreArgs {
   float* lse2;       // [hq][len]  lse * log2(e)
   int len, hq;
   int ls;            // elements between heads in lse / delta / lse2
+  const void* q;     // bf16 only: [len][hq][D] bf16
+  void* q16;         // bf16 only: [len][hq][D] half copy of q
+  void* do16;        // bf16 only: [len][hq][D] half copy of dout
 };
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hipStream_t st);
 
-// Backward ring step against one K/V block.
+// Backward ring step against one K/V block.  bf16 path: q and dout are the
+// half copies; the dK/dV kernel reads k/v as bf16 and writes their half copies
+// to k16/v16, which the dQ kernel then reads as its k/v.
 struct BwdArgs {
   const void* q;     // [len][hq][D]
   const void* k;     // [len][hkv][D]
   const void* v;
   const void* dout;  // [len][hq][D]
+  void* k16;         // bf16 dK/dV kernel: [len][hkv][D] half copy of k (written)
+  void* v16;         // bf16 dK/dV kernel: [len][hkv][D] half copy of v (written)
   const float* lse;  // [hq][len]
   const float* delta;  // [hq][len]
   const float* lse2;   // [hq][len] lse * log2(e)

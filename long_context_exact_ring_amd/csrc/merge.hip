@@ -8,7 +8,8 @@
 //
 // Backward preprocess: Delta_i = sum_d dout_i * out_i for every (head, row),
 // the row term of dS = P * (dP - Delta), and lse in log2 units (the exponent
-// offset the backward kernels use).  One wavefront per (row, head).
+// offset the backward kernels use); for bf16 inputs also the half copies of q
+// and dout that the bf16 backward kernels contract.  One wavefront per (row, head).
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -78,6 +79,21 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
       dv = dp[j];
     }
     acc = __builtin_fmaf(dv, op[j], acc);
+  }
+  if constexpr (sizeof(T) == 2) {  // half copies of q and dout (exact for |x| in [2^-14, 65504])
+    static_assert(PER == 1 || PER == 2, "one 32-bit word per lane and tensor");
+    const T* qp = reinterpret_cast<const T*>(a.q) + rh * D + lane * PER;
+    T* q16 = reinterpret_cast<T*>(a.q16) + rh * D + lane * PER;
+    T* d16 = reinterpret_cast<T*>(a.do16) + rh * D + lane * PER;
+    if constexpr (PER == 2) {
+      const uint32_t qw = *reinterpret_cast<const uint32_t*>(qp);
+      const uint32_t dw = *reinterpret_cast<const uint32_t*>(dp);
+      *reinterpret_cast<uint32_t*>(q16) = bf16x2_to_f16x2(qw);
+      *reinterpret_cast<uint32_t*>(d16) = bf16x2_to_f16x2(dw);
+    } else {
+      q16[0] = (T)bf16x2_to_f16x2((uint32_t)qp[0]);
+      d16[0] = (T)bf16x2_to_f16x2((uint32_t)dp[0]);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);

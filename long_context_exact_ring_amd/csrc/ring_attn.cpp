@@ -18,12 +18,8 @@
 // rank's own block comes first and is the masked diagonal).
 //
 // In the backward, the dK/dV and dQ kernels of a round read the same K/V
-// block and write different outputs.  With RA_BWD_TWO_STREAMS the dQ chain
-// runs on a second library-owned stream, forked from the main stream at every
-// round: the two kernels of a round share the GPU, and each fills the CUs the
-// other leaves idle while its last workgroups drain.  A staging buffer is then
-// refilled only after both kernels that read it are done, and the main stream
-// joins the dQ chain before the call's work ends.
+// block and write different outputs; with bf16 inputs the dK/dV kernel also
+// writes the half copy of the block that the dQ kernel after it reads.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,14 +36,6 @@
 #include "../../include/ring_attn.h"
 #include "kernels.h"
 #include "ring_host.h"
-
-#ifndef RA_BWD_TWO_STREAMS
-// 1: the backward's dQ chain runs on a second stream next to the dK/dV chain
-// (+1.2% on a causal 128k step, +2.2% in the zig-zag layout).  Off: with the
-// two kernels sharing the GPU, each one's event-timed duration spans the
-// other's work too, so per-kernel durations no longer describe the kernels.
-#define RA_BWD_TWO_STREAMS 0
-#endif
 
 namespace ra {
 
@@ -140,13 +128,15 @@ struct Ctx {
   hipStream_t side = nullptr;
   hipEvent_t ev_entry = nullptr, ev_side_end = nullptr;
   hipEvent_t ev_copied[2] = {nullptr, nullptr}, ev_done[2] = {nullptr, nullptr};
-  hipStream_t aux = nullptr;  // backward: the dQ chain
-  hipEvent_t ev_fork[2] = {nullptr, nullptr}, ev_aux_done[2] = {nullptr, nullptr}, ev_aux_end = nullptr;
+  hipEvent_t ev_last = nullptr;  // end of the last call on this device (on that call's stream)
+  bool last_valid = false;
   void* stage = nullptr;  // [kbuf0 | kbuf1 | vbuf0 | vbuf1]
   size_t stage_cap = 0;
   bool stage_owned = true;  // false: caller memory from ring_attn_set_workspace
-  float* delta = nullptr;
-  size_t delta_cap = 0;
+  // backward workspace: row terms [delta | lse2] (fp32), then for bf16 inputs
+  // the half copies [q16 | do16] of the query block and [k16 | v16] of one K/V block
+  void* bwd = nullptr;
+  size_t bwd_cap = 0;
   float* dec = nullptr;  // decode partials
   size_t dec_cap = 0;
   void* ffn = nullptr;   // blockwise feedforward intermediate (one row chunk)
@@ -172,15 +162,9 @@ static int get_ctx(Ctx** out) {
   c->device = dev;
   hipError_t e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
   hipEvent_t* evs[] = {&c->ev_entry, &c->ev_side_end, &c->ev_copied[0], &c->ev_copied[1], &c->ev_done[0],
-                       &c->ev_done[1]};
+                       &c->ev_done[1],  &c->ev_last};
   for (hipEvent_t* ev : evs)
     if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
-  if (RA_BWD_TWO_STREAMS) {  // the backward's dQ stream and its fork/join events
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
-    hipEvent_t* aux_evs[] = {&c->ev_fork[0], &c->ev_fork[1], &c->ev_aux_done[0], &c->ev_aux_done[1], &c->ev_aux_end};
-    for (hipEvent_t* ev : aux_evs)
-      if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
-  }
   if (e != hipSuccess) {
     delete c;
     return fail(RA_ERR_HIP, "creating side stream/events: %s", hipGetErrorString(e));
@@ -189,6 +173,24 @@ static int get_ctx(Ctx** out) {
   *out = c;
   return RA_OK;
 }
+
+// Calls on one device share its staging and workspace buffers, so they run one
+// after another on the GPU even when issued on different streams: a call's
+// stream first waits for the end of the previous call (an event recorded on
+// that call's stream), and the call records its own end when it is done
+// enqueueing.  Enqueueing itself is serialised by the library mutex.
+struct CallOrder {
+  Ctx* c;
+  hipStream_t st;
+  CallOrder(Ctx* c_, hipStream_t s) : c(c_), st(s) {}
+  int begin() {
+    if (c->last_valid) RA_HIP(hipStreamWaitEvent(st, c->ev_last, 0));
+    return RA_OK;
+  }
+  ~CallOrder() {
+    if (hipEventRecord(c->ev_last, st) == hipSuccess) c->last_valid = true;
+  }
+};
 
 static int ensure_stage(Ctx* c, size_t bytes) {
   if (c->stage_cap >= bytes) return RA_OK;
@@ -210,22 +212,41 @@ static int ensure_stage(Ctx* c, size_t bytes) {
   return RA_OK;
 }
 
-static int ensure_delta(Ctx* c, size_t bytes) {
-  if (c->delta_cap >= bytes) return RA_OK;
-  if (c->delta) {
+static int ensure_bwd(Ctx* c, size_t bytes) {
+  if (c->bwd_cap >= bytes) return RA_OK;
+  if (c->bwd) {
     RA_HIP(hipDeviceSynchronize());
-    RA_HIP(hipFree(c->delta));
-    c->delta = nullptr;
-    c->delta_cap = 0;
+    RA_HIP(hipFree(c->bwd));
+    c->bwd = nullptr;
+    c->bwd_cap = 0;
   }
-  if (hipMalloc((void**)&c->delta, bytes) != hipSuccess) {
+  if (hipMalloc(&c->bwd, bytes) != hipSuccess) {
     (void)hipGetLastError();
-    c->delta = nullptr;
-    return fail(RA_ERR_OOM, "could not allocate %zu bytes for the backward row terms", bytes);
+    c->bwd = nullptr;
+    return fail(RA_ERR_OOM, "could not allocate %zu bytes of backward workspace", bytes);
   }
-  c->delta_cap = bytes;
+  c->bwd_cap = bytes;
   return RA_OK;
 }
+
+// Regions of the backward workspace, each starting on a 256-byte boundary.
+struct BwdLayout {
+  size_t delta, lse2, q16, do16, k16, v16, total;
+  explicit BwdLayout(const Shape& sh) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    delta = 0;
+    lse2 = up(sh.lse_bytes());
+    q16 = lse2 + up(sh.lse_bytes());
+    if (sh.elem_bytes == 2) {  // half copies: 2 bytes per element, the inputs' own layouts
+      do16 = q16 + up(sh.q_bytes());
+      k16 = do16 + up(sh.q_bytes());
+      v16 = k16 + up(sh.kv_bytes());
+      total = v16 + up(sh.kv_bytes());
+    } else {
+      do16 = k16 = v16 = total = q16;
+    }
+  }
+};
 
 static int ensure_dec(Ctx* c, size_t bytes) {
   if (c->dec_cap >= bytes) return RA_OK;
@@ -331,13 +352,10 @@ static bool log_schedule() {
 }
 
 // ------------------------------------------------------------------ the ring pipeline
-// step_fn(s, j, k_ptr, v_ptr) launches round s's kernels on `stream`.  With
-// `aux_done`, step_fn also reads the round's staging buffer from another stream
-// and records aux_done[s & 1] there after its last reader; the buffer is then
-// refilled only after that event as well.
+// step_fn(s, j, k_ptr, v_ptr) launches round s's kernels on `stream`.
 template <typename StepFn>
 static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* const* vb,
-                    hipStream_t stream, StepFn&& step_fn, const hipEvent_t* aux_done = nullptr) {
+                    hipStream_t stream, StepFn&& step_fn) {
   const std::vector<int> steps = ring_schedule(sh.rank, sh.n_blocks, sh.schedule_causal());
   const int S = (int)steps.size();
   const size_t kvb = sh.kv_bytes();
@@ -382,7 +400,6 @@ static int run_ring(Ctx* c, const Shape& sh, const void* const* kb, const void* 
     if (s + 2 < S) {
       RA_HIP(hipEventRecord(c->ev_done[b], stream));
       RA_HIP(hipStreamWaitEvent(c->side, c->ev_done[b], 0));
-      if (aux_done) RA_HIP(hipStreamWaitEvent(c->side, aux_done[b], 0));
       if ((st = issue_copy(s + 2)) != RA_OK) return st;
     }
   }
@@ -419,6 +436,8 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   std::lock_guard<std::mutex> lk(g_mu);
   Ctx* c = nullptr;
   if ((st = get_ctx(&c)) != RA_OK) return st;
+  CallOrder order(c, stream);
+  if ((st = order.begin()) != RA_OK) return st;
   ++g_prof_call;
   const int group = sh.heads / sh.kv_heads;
   const int hpw = heads_per_block(group, fwd_waves_per_block(sh.elem_bytes));
@@ -514,27 +533,39 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   std::lock_guard<std::mutex> lk(g_mu);
   Ctx* c = nullptr;
   if ((st = get_ctx(&c)) != RA_OK) return st;
+  CallOrder order(c, stream);
+  if ((st = order.begin()) != RA_OK) return st;
   ++g_prof_call;
   // staging first: a caller workspace that is too small must fail before anything is enqueued
   if (ring_schedule(sh.rank, sh.n_blocks, sh.schedule_causal()).size() > 1 &&
       (st = ensure_stage(c, 4 * sh.kv_bytes())) != RA_OK)
     return st;
-  if ((st = ensure_delta(c, 2 * sh.lse_bytes())) != RA_OK) return st;
-  float* lse2 = c->delta + (size_t)sh.block_len * sh.heads;
+  const BwdLayout L(sh);
+  if ((st = ensure_bwd(c, L.total)) != RA_OK) return st;
+  char* ws = static_cast<char*>(c->bwd);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  const bool half = sh.elem_bytes == 2;  // bf16 inputs: the kernels contract half copies
+  void* q16 = half ? ws + L.q16 : nullptr;
+  void* do16 = half ? ws + L.do16 : nullptr;
+  char* k16 = half ? ws + L.k16 : nullptr;
+  char* v16 = half ? ws + L.v16 : nullptr;
   {
-    BwdPreArgs p{dout, out, lse, c->delta, lse2, sh.block_len, sh.heads, sh.block_len};
+    BwdPreArgs p{dout, out, lse, delta, lse2, sh.block_len, sh.heads, sh.block_len, q, q16, do16};
     ProfScope ps(KIND_PRE, stream);
     RA_HIP(launch_bwd_pre(p, sh.elem_bytes, sh.head_dim, stream));
   }
+  const void* qk = half ? q16 : q;      // what the kernels read as q and dout
+  const void* dok = half ? do16 : dout;
   const float scale = rsqrt_dim(sh.head_dim);
   const int group = sh.heads / sh.kv_heads;
   const int hpw =
       heads_per_block(group, sh.elem_bytes == 2 ? bwd_bf16_waves_per_block() : bwd_dq_waves_per_block());
   BwdArgs base{};
-  base.q = q;
-  base.dout = dout;
+  base.q = qk;
+  base.dout = dok;
   base.lse = lse;
-  base.delta = c->delta;
+  base.delta = delta;
   base.lse2 = lse2;
   base.dq = dq;
   base.len = sh.block_len;
@@ -551,12 +582,18 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
     RA_HIP(launch_bwd_dkdv(a, nsub, sh.elem_bytes, sh.head_dim, stream));
     return RA_OK;
   };
-  // the dQ chain runs on c->aux (RA_BWD_TWO_STREAMS), forked from `stream` at every round
-  hipStream_t dq_stream = RA_BWD_TWO_STREAMS ? c->aux : stream;
   auto launch_dq = [&](const BwdArgs* a, int nsub) -> int {
-    ProfScope ps(KIND_DQ, dq_stream);
-    RA_HIP(launch_bwd_dq(a, nsub, sh.elem_bytes, sh.head_dim, dq_stream));
+    ProfScope ps(KIND_DQ, stream);
+    RA_HIP(launch_bwd_dq(a, nsub, sh.elem_bytes, sh.head_dim, stream));
     return RA_OK;
+  };
+  // bf16: the dQ kernel reads the half copy of the block that the dK/dV kernel wrote
+  auto for_dq = [&](BwdArgs a) {
+    if (half) {
+      a.k = a.k16;
+      a.v = a.v16;
+    }
+    return a;
   };
   bool first_half[2] = {true, true};
   auto bwd_round = [&](int s, int j, const void* kp, const void* vp) -> int {
@@ -564,16 +601,22 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       BwdArgs a = base;
       a.k = kp;
       a.v = vp;
+      a.k16 = k16;
+      a.v16 = v16;
       a.dk = dkb[j];
       a.dv = dvb[j];
       a.diag = (sh.causal && j == sh.rank) ? 1 : 0;
       a.first = (s == 0) ? 1 : 0;
       int st2 = launch_dkdv(&a, 1);
-      return st2 != RA_OK ? st2 : launch_dq(&a, 1);
+      if (st2 != RA_OK) return st2;
+      const BwdArgs b = for_dq(a);
+      return launch_dq(&b, 1);
     }
     // zig-zag: the (query half u, key half v) pairs that attend.  dK/dV launches take the
     // key halves of one query half as two sub-problems (they write different dK/dV rows);
-    // dQ launches take the query halves of one key half (different dQ rows).
+    // dQ launches take the query halves of one key half (different dQ rows).  Every live
+    // key half is covered by some dK/dV launch, which writes its half copy before the
+    // dQ launches of the round read it.
     const int h = sh.block_len / 2;
     const size_t qrow = (size_t)sh.heads * sh.head_dim, krow = (size_t)sh.kv_heads * sh.head_dim;
     BwdArgs pa[2][2];
@@ -584,14 +627,16 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
         live[u][v] = !(sh.causal && kc > qc);
         BwdArgs& a = pa[u][v];
         a = base;
-        a.q = static_cast<const char*>(q) + u * h * qrow * sh.elem_bytes;
-        a.dout = static_cast<const char*>(dout) + u * h * qrow * sh.elem_bytes;
+        a.q = static_cast<const char*>(qk) + u * h * qrow * sh.elem_bytes;
+        a.dout = static_cast<const char*>(dok) + u * h * qrow * sh.elem_bytes;
         a.lse = lse + (size_t)u * h;
-        a.delta = c->delta + (size_t)u * h;
+        a.delta = delta + (size_t)u * h;
         a.lse2 = lse2 + (size_t)u * h;
         a.dq = dq + u * h * qrow;
         a.k = static_cast<const char*>(kp) + v * h * krow * sh.elem_bytes;
         a.v = static_cast<const char*>(vp) + v * h * krow * sh.elem_bytes;
+        a.k16 = half ? k16 + v * h * krow * 2 : nullptr;
+        a.v16 = half ? v16 + v * h * krow * 2 : nullptr;
         a.dk = dkb[j] + v * h * krow;
         a.dv = dvb[j] + v * h * krow;
         a.len = h;
@@ -612,7 +657,7 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       for (int u = 0; u < 2; ++u)
         if (live[u][v]) {
           BwdArgs& a = sub[nsub++];
-          a = pa[u][v];
+          a = for_dq(pa[u][v]);
           a.first = first_half[u] ? 1 : 0;  // dQ rows of half u: written by the first, then accumulated
           first_half[u] = false;
         }
@@ -622,21 +667,7 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
     }
     return RA_OK;
   };
-  auto step = [&](int s, int j, const void* kp, const void* vp) -> int {
-    if (RA_BWD_TWO_STREAMS) {  // everything enqueued on `stream` so far (copy waits, bwd_pre) precedes this round's dQ
-      RA_HIP(hipEventRecord(c->ev_fork[s & 1], stream));
-      RA_HIP(hipStreamWaitEvent(dq_stream, c->ev_fork[s & 1], 0));
-    }
-    int rc = bwd_round(s, j, kp, vp);
-    if (rc == RA_OK && RA_BWD_TWO_STREAMS) RA_HIP(hipEventRecord(c->ev_aux_done[s & 1], dq_stream));
-    return rc;
-  };
-  int rc = run_ring(c, sh, kb, vb, stream, step, RA_BWD_TWO_STREAMS ? c->ev_aux_done : nullptr);
-  if (rc == RA_OK && RA_BWD_TWO_STREAMS) {
-    RA_HIP(hipEventRecord(c->ev_aux_end, dq_stream));
-    RA_HIP(hipStreamWaitEvent(stream, c->ev_aux_end, 0));
-  }
-  return rc;
+  return run_ring(c, sh, kb, vb, stream, bwd_round);
 }
 
 int merge_impl(const float* oa, const float* la, const float* obp, const float* lb, int rows, int heads,
@@ -793,6 +824,8 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   Ctx* c = nullptr;
   int st = get_ctx(&c);
   if (st != RA_OK) return st;
+  CallOrder order(c, stream);
+  if ((st = order.begin()) != RA_OK) return st;
   if ((st = ensure_dec(c, need)) != RA_OK) return st;
   DecodeArgs a{};
   a.q = q;
@@ -858,6 +891,8 @@ int ffn_impl(const void* x, const void* w1, const float* b1, const void* w2, con
   Ctx* c = nullptr;
   int st = get_ctx(&c);
   if (st != RA_OK) return st;
+  CallOrder order(c, stream);
+  if ((st = order.begin()) != RA_OK) return st;
   if ((st = ensure_ffn(c, (size_t)chunk * ffn * 2)) != RA_OK) return st;
   ++g_prof_call;
   for (int r0 = 0; r0 < rows; r0 += chunk) {
@@ -925,16 +960,14 @@ void shutdown_all() {
     (void)hipSetDevice(c->device);
     (void)hipDeviceSynchronize();
     if (c->stage && c->stage_owned) (void)hipFree(c->stage);
-    if (c->delta) (void)hipFree(c->delta);
+    if (c->bwd) (void)hipFree(c->bwd);
     if (c->dec) (void)hipFree(c->dec);
     if (c->ffn) (void)hipFree(c->ffn);
-    hipEvent_t evs[] = {c->ev_entry,   c->ev_side_end,  c->ev_copied[0],  c->ev_copied[1],
-                        c->ev_done[0], c->ev_done[1],   c->ev_fork[0],    c->ev_fork[1],
-                        c->ev_aux_done[0], c->ev_aux_done[1], c->ev_aux_end};
+    hipEvent_t evs[] = {c->ev_entry,   c->ev_side_end, c->ev_copied[0], c->ev_copied[1],
+                        c->ev_done[0], c->ev_done[1],  c->ev_last};
     for (hipEvent_t e : evs)
       if (e) (void)hipEventDestroy(e);
     if (c->side) (void)hipStreamDestroy(c->side);
-    if (c->aux) (void)hipStreamDestroy(c->aux);
     (void)hipSetDevice(prev);
     delete c;
   }

@@ -23,7 +23,7 @@ definition softmax(Q K^T / sqrt(d)) V, written out in fp64 (``dense``).  The
 blockwise/online form (``ring``) follows the pages' steps and exists to pin
 the definition against the pages' invariants.
 """
-from .dense import (attention_fwd, attention_bwd, brute_force_fwd, positions_for_block,
+from .dense import (attention_fwd, attention_bwd, attention_bwd_keys, brute_force_fwd, positions_for_block,
                     sampled_rows_fwd)
 from .ring import (ring_steps, simulate_ring, ring_forward, online_block_forward,
                    merge_partials, merge_partials_scalar, zigzag_positions, visible_pairs_per_rank)
@@ -31,7 +31,7 @@ from .decode import decode_forward, decode_by_partials
 from .ffn import ffn_blockwise, ffn_forward, gelu
 
 __all__ = [
-    "attention_fwd", "attention_bwd", "brute_force_fwd", "positions_for_block",
+    "attention_fwd", "attention_bwd", "attention_bwd_keys", "brute_force_fwd", "positions_for_block",
     "sampled_rows_fwd", "ring_steps", "simulate_ring", "ring_forward",
     "online_block_forward", "merge_partials", "merge_partials_scalar",
     "decode_forward", "decode_by_partials", "zigzag_positions", "visible_pairs_per_rank",

@@ -46,22 +46,29 @@ def _row_chunk(n_keys: int) -> int:
 
 def _scores(qh: np.ndarray, kg: np.ndarray, scale: float, causal: bool,
             q_pos: np.ndarray, k_pos: np.ndarray) -> np.ndarray:
-    s = (qh @ kg.T) * scale
-    if causal:
-        s = np.where(k_pos[None, :] <= q_pos[:, None], s, -np.inf)
+    s = qh @ kg.T
+    s *= scale
+    if causal and s.size:
+        # keys at or before the chunk's first query position are visible to every row,
+        # so only the other columns need the per-element test (same values, less work)
+        cols = np.nonzero(k_pos > q_pos.min())[0]
+        if cols.size:
+            s[:, cols] = np.where(k_pos[cols][None, :] <= q_pos[:, None], s[:, cols], -np.inf)
     return s
 
 
 def _softmax_rows(s: np.ndarray):
-    """Two-pass softmax over rows; returns (P, lse). Empty rows give P = 0, lse = -inf."""
+    """Two-pass softmax over rows, in place on ``s``; returns (P, lse). Empty rows give
+    P = 0, lse = -inf."""
     m = s.max(axis=1)
     finite = np.isfinite(m)
     m_safe = np.where(finite, m, 0.0)
-    p = np.exp(s - m_safe[:, None])          # exp(-inf) = 0 for masked entries
+    s -= m_safe[:, None]
+    p = np.exp(s, out=s)                     # exp(-inf) = 0 for masked entries
     l = p.sum(axis=1)
     with np.errstate(divide="ignore"):
         lse = np.where(finite, m_safe + np.log(np.where(finite, l, 1.0)), -np.inf)
-    p = np.where(finite[:, None], p / np.where(finite, l, 1.0)[:, None], 0.0)
+    p /= np.where(finite, l, 1.0)[:, None]   # an empty row is all zeros already
     return p, lse
 
 
@@ -165,6 +172,47 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
             dq[r0:r1, h, :] = (ds @ kg[:kv]) * scale
             dk[:kv, g, :] += (ds.T @ qh) * scale
     return dq, dk, dv, out, lse
+
+
+def attention_bwd_keys(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, *, causal: bool,
+                       keys: np.ndarray, q_pos: Optional[np.ndarray] = None,
+                       k_pos: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """dK and dV at the chosen key indices ``keys`` only, summed over every query row.
+
+    The same definition as ``attention_bwd`` restricted to a few columns of P:
+    every row's output and lse come from its full visible key set (the
+    forward above), Delta_i = dO_i . O_i, and then for the chosen keys t only
+    P_it = exp(S_it - lse_i), dS_it = P_it (dO_i . v_t - Delta_i),
+    dV_t = sum_i P_it dO_i, dK_t = sum_i dS_it q_i / sqrt(d) (summed over the
+    query heads of a grouped K/V head).  Returns ``dk, dv [len(keys), Hkv, d]``.
+    """
+    n, hq, d = q.shape
+    m, hkv, _ = k.shape
+    q_pos, k_pos = _defaults(n, m, q_pos, k_pos)
+    keys = np.asarray(keys, dtype=np.int64)
+    group = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    out, lse = attention_fwd(q, k, v, causal=causal, q_pos=q_pos, k_pos=k_pos)
+    dk = np.zeros((keys.size, hkv, d), dtype=np.float64)
+    dv = np.zeros((keys.size, hkv, d), dtype=np.float64)
+    chunk = _row_chunk(keys.size)
+    for h in range(hq):
+        g = h // group
+        kt = np.asarray(k[keys, g, :], dtype=np.float64)
+        vt = np.asarray(v[keys, g, :], dtype=np.float64)
+        for r0 in range(0, n, chunk):
+            r1 = min(n, r0 + chunk)
+            qh = np.asarray(q[r0:r1, h, :], dtype=np.float64)
+            doh = np.asarray(dout[r0:r1, h, :], dtype=np.float64)
+            s = _scores(qh, kt, scale, causal, q_pos[r0:r1], k_pos[keys])
+            l = lse[h, r0:r1]
+            ok = np.isfinite(l)  # rows with no visible key contribute nothing
+            p = np.where(ok[:, None], np.exp(s - np.where(ok, l, 0.0)[:, None]), 0.0)
+            delta = np.sum(doh * out[r0:r1, h, :], axis=1)
+            ds = p * (doh @ vt.T - delta[:, None])
+            dv[:, g, :] += p.T @ doh
+            dk[:, g, :] += (ds.T @ qh) * scale
+    return dk, dv
 
 
 def brute_force_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, causal: bool,

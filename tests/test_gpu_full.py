@@ -4,9 +4,14 @@ Every workload's GPU result is computed in full; the fp64 oracle is evaluated
 on sampled query rows and heads (each sampled output is exact attention over
 all of that row's visible keys), and for the backward on whole heads.
 """
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import long_context_exact_ring_amd as ra
 import oracle
@@ -64,20 +69,121 @@ def test_full_noncausal_64k_h16_d64():
     check_fwd_sampled(w, 0, out, lse, kblk, vblk, heads=list(range(w.heads)))
 
 
+def dense_rows(c):
+    """First and last 64 rows plus every 16th row of a query block."""
+    return np.unique(np.concatenate([np.arange(64), np.arange(c - 64, c), np.arange(0, c, 16)])).astype(np.int64)
+
+
+def _pool(fn, items):
+    """Independent oracle calls side by side: numpy's matrix products and elementwise
+    loops release the GIL, so one thread per core, each with a single-threaded BLAS."""
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
+
+
 def test_full_causal_128k_all_ranks():
+    """The headline workload's forward, as bench.py runs it: every rank's share against
+    the oracle on every head, at the first and last 64 rows and every 16th row."""
     require_gpu()
     w = WORKLOADS["causal_128k_h32_d128"]
     log(f"workload {w.name}")
+    t0 = time.time()
+    c = w.block_len
     kblk, vblk = kv_blocks(w)
     kb = [up(x, w.dtype) for x in kblk]
     vb = [up(x, w.dtype) for x in vblk]
-    results = {}
+    rows = dense_rows(c)
+    got = {}
     for r in w.ranks:  # every rank's share, as the bench step runs them
         q = up(gen_block(w.seed, "q", r, w.block_len, w.heads, w.head_dim, w.dtype), w.dtype)
-        results[r] = ra.fwd(q, kb, vb, causal=True, rank=r)
+        out, lse = ra.fwd(q, kb, vb, causal=True, rank=r)
+        idx = torch.from_numpy(rows).cuda()
+        got[r] = (out[idx].cpu(), lse[:, idx].cpu())
     torch.cuda.synchronize()
-    for r in (0, 7, 15):
-        check_fwd_sampled(w, r, *results[r], kblk, vblk, heads=[0, 17, 31])
+    k_all, v_all = np.concatenate(kblk), np.concatenate(vblk)
+
+    qs = {r: gen_block(w.seed, "q", r, c, w.heads, w.head_dim, w.dtype)[rows] for r in w.ranks}
+
+    def ref(task):  # one rank and one head (MHA: K/V head = query head)
+        r, h = task
+        nvis = (r + 1) * c
+        return oracle.sampled_rows_fwd(qs[r][:, [h]], r * c + rows, k_all[:nvis, [h]], v_all[:nvis, [h]],
+                                       causal=True)
+
+    tasks = [(r, h) for r in reversed(w.ranks) for h in range(w.heads)]  # longest first
+    refs = dict(zip(tasks, _pool(ref, tasks)))
+    for r in w.ranks:
+        o_ref = np.concatenate([refs[(r, h)][0] for h in range(w.heads)], axis=1)
+        l_ref = np.concatenate([refs[(r, h)][1] for h in range(w.heads)], axis=0)
+        compare(f"{w.name} rank {r} out ({rows.size} rows x {w.heads} heads)", got[r][0], o_ref, w.dtype)
+        compare(f"{w.name} rank {r} lse", got[r][1], l_ref, w.dtype)
+    log(f"  {time.time() - t0:.1f}s")
+
+
+def test_full_backward_causal_128k():
+    """The headline workload's backward, as bench.py runs it (forward and backward of every
+    rank, dK/dV accumulated over the ranks).  dQ: sampled rows of every rank, every head.
+    dK/dV: heads 0 and 31 at sampled keys of blocks 0 (seen by every row), 7 and 15,
+    against the oracle's own forward over all 131072 rows of those heads."""
+    require_gpu()
+    w = WORKLOADS["causal_128k_h32_d128"]
+    log(f"workload {w.name} backward")
+    t0 = time.time()
+    c, D, H, d = w.block_len, w.n_blocks, w.heads, w.head_dim
+    kblk, vblk = kv_blocks(w)
+    kb = [up(x, w.dtype) for x in kblk]
+    vb = [up(x, w.dtype) for x in vblk]
+    qs = [gen_block(w.seed, "q", r, c, H, d, w.dtype) for r in range(D)]
+    dos = [gen_block(w.seed, "do", r, c, H, d, w.dtype) for r in range(D)]
+    dkb = [torch.zeros((c, w.kv_heads, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+    dvb = [torch.zeros((c, w.kv_heads, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+    qrows = {r: sample_rows(c, n_random=4, seed=100 + r) for r in range(D)}
+    dq_got = {}
+    for r in range(D):
+        qd, dod = up(qs[r], w.dtype), up(dos[r], w.dtype)
+        o, l = ra.fwd(qd, kb, vb, causal=True, rank=r)
+        g, _, _ = ra.bwd(qd, kb, vb, o, dod, l, causal=True, rank=r, dk_blocks=dkb, dv_blocks=dvb)
+        dq_got[r] = g[torch.from_numpy(qrows[r]).cuda()].cpu()
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    keys = np.array([0, 1, 17, c // 2, c - 1, 7 * c, 7 * c + 4095, D * c - 2, D * c - 1], dtype=np.int64)
+    dk_got = torch.cat(dkb, 0)[torch.from_numpy(keys).cuda()][:, heads].cpu()
+    dv_got = torch.cat(dvb, 0)[torch.from_numpy(keys).cuda()][:, heads].cpu()
+    k_all, v_all = np.concatenate(kblk), np.concatenate(vblk)
+
+    def dq_ref(r):
+        rows = qrows[r]
+        nvis = (r + 1) * c
+        g, _, _, _, _ = oracle.attention_bwd(qs[r][rows], k_all[:nvis], v_all[:nvis], dos[r][rows], causal=True,
+                                             q_pos=r * c + rows)
+        return g
+
+    for r, ref in zip(range(D), _pool(dq_ref, list(range(D)))):
+        compare(f"dq rank {r} ({qrows[r].size} rows x {H} heads)", dq_got[r], ref, w.dtype)
+
+    # dK/dV at the chosen keys sum over every row of the head: split the rows into ranges
+    # (each range's sum is exact), add the ranges' contributions
+    q_h = np.concatenate(qs)[:, heads]
+    do_h = np.concatenate(dos)[:, heads]
+    k_h, v_h = k_all[:, heads], v_all[:, heads]
+    step = 8192
+
+    def dkdv_part(task):  # one row range of one head
+        r0, i = task
+        r1 = min(D * c, r0 + step)
+        return oracle.attention_bwd_keys(q_h[r0:r1, [i]], k_h[:, [i]], v_h[:, [i]], do_h[r0:r1, [i]], causal=True,
+                                         keys=keys, q_pos=np.arange(r0, r1))
+
+    tasks = [(r0, i) for r0 in reversed(range(0, D * c, step)) for i in range(len(heads))]  # longest first
+    parts = dict(zip(tasks, _pool(dkdv_part, tasks)))
+    dk_ref = np.concatenate([np.sum([parts[(r0, i)][0] for r0 in range(0, D * c, step)], axis=0)
+                             for i in range(len(heads))], axis=1)
+    dv_ref = np.concatenate([np.sum([parts[(r0, i)][1] for r0 in range(0, D * c, step)], axis=0)
+                             for i in range(len(heads))], axis=1)
+    compare(f"dk heads {heads} at {keys.size} keys", dk_got, dk_ref, w.dtype)
+    compare(f"dv heads {heads} at {keys.size} keys", dv_got, dv_ref, w.dtype)
+    log(f"  {time.time() - t0:.1f}s")
 
 
 def test_full_causal_512k_gqa_rank7():

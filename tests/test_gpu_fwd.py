@@ -240,10 +240,10 @@ def test_mfma_rate_probe_is_plausible():
 def test_binding_refuses_strided_views():
     """The library reads dense row-major buffers; a transposed view must be refused, not misread."""
     require_gpu()
-    q = torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((2, 64, 64), dtype=torch.bfloat16, device="cuda").transpose(0, 1)  # [64, 2, 64], strided
     kb = [torch.zeros((64, 2, 64), dtype=torch.bfloat16, device="cuda")]
     with pytest.raises(ValueError, match="contiguous"):
-        ra.fwd(q.transpose(0, 1), kb, kb, causal=False, rank=0)
+        ra.fwd(q, kb, kb, causal=False, rank=0)
 
 
 def test_shutdown_then_reuse_gives_identical_results():
@@ -298,3 +298,50 @@ def test_calls_order_against_the_callers_stream():
         o, l = ra.fwd(qd, kb2, vb2, causal=False, rank=1)
     s.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(l, l_ref)
+
+
+def test_calls_on_two_streams_serialise():
+    """Calls issued on two streams of one device share the library's staging and
+    workspace buffers; the library orders each call after the previous one, so the
+    interleaved calls give bit-identical results to the same calls run serially.
+    The first stream is held busy by a bounded spin, so without that ordering the
+    second stream's calls would refill the shared buffers under the first's."""
+    require_gpu()
+    dtype, d, h, c, D = "bf16", 128, 4, 512, 5
+    q, k, v = _inputs(73, dtype, d, h, h, c, D)
+    do = gen_small(73, (c * D, h, d), dtype, 1.0, 3)
+    kb = [dev(k[j * c:(j + 1) * c], dtype) for j in range(D)]
+    vb = [dev(v[j * c:(j + 1) * c], dtype) for j in range(D)]
+    ranks = (1, 3)
+    qs = {r: dev(q[r * c:(r + 1) * c], dtype) for r in ranks}
+    dos = {r: dev(do[r * c:(r + 1) * c], dtype) for r in ranks}
+
+    def outputs():
+        return {r: dict(o=torch.empty((c, h, d), device="cuda"), l=torch.empty((h, c), device="cuda"),
+                        dq=torch.empty((c, h, d), device="cuda"),
+                        dk=[torch.zeros((c, h, d), device="cuda") for _ in range(D)],
+                        dv=[torch.zeros((c, h, d), device="cuda") for _ in range(D)]) for r in ranks}
+
+    def call(r, res, stream=None):
+        x = res[r]
+        ra.fwd(qs[r], kb, vb, causal=False, rank=r, out=x["o"], lse=x["l"], stream=stream)
+        ra.bwd(qs[r], kb, vb, x["o"], dos[r], x["l"], causal=False, rank=r, dq=x["dq"], dk_blocks=x["dk"],
+               dv_blocks=x["dv"], stream=stream)
+
+    serial = outputs()
+    for r in ranks:
+        call(r, serial)
+    inter = outputs()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s1):
+        torch.cuda._sleep(20_000_000)  # bounded spin: the first call starts a few ms late
+    call(ranks[0], inter, stream=s1)
+    call(ranks[1], inter, stream=s2)
+    torch.cuda.synchronize()
+    for r in ranks:
+        for key in ("o", "l", "dq"):
+            assert torch.equal(serial[r][key], inter[r][key]), f"rank {r} {key} differs"
+        for j in range(D):
+            assert torch.equal(serial[r]["dk"][j], inter[r]["dk"][j]), f"rank {r} dk[{j}] differs"
+            assert torch.equal(serial[r]["dv"][j], inter[r]["dv"][j]), f"rank {r} dv[{j}] differs"

@@ -6,15 +6,12 @@ put back in sequence order and compared with dense fp64 causal attention.
 The per-rank launch counts show the balance: every rank runs the same
 number of half-size steps.
 
-The shapes keep the gradients at the magnitudes of the benchmark workloads
-(max |dV| about 6).  The absolute bf16 bound is met by a relative error of
-about 1e-3 (P and dO enter the dV product rounded to bf16).  Under the causal
-mask, key 0 collects weight from every row of every grouped head, so a
-4-way group over 600 rows drives |dV| to about 10, and the same relative
-error then crosses 1e-2 in absolute terms.  Likewise, with one token per
-chunk and a shared K/V head, dQ has so few terms that rounding dS to bf16
-alone costs 1.02e-2 (an fp64 emulation of that rounding reproduces the
-kernel's error), so that case uses two K/V heads.
+The shapes include large gradients: under the causal mask key 0 collects
+weight from every row of every grouped head, so a 4-way group over 600 rows
+puts |dV| near 6.5, and with one token per chunk and a shared K/V head dQ has
+so few terms that each rounded dS counts.  Rounding P and dS to bf16 for the
+matrix core would cost 1.0e-2 to 1.1e-2 on those shapes (an fp64 emulation
+of that rounding); the backward rounds them to half precision instead.
 """
 import numpy as np
 import pytest
@@ -33,11 +30,10 @@ CASES = [
     (128, 4, 2, 200, 3),   # chunks of 100 tokens: ragged tiles, GQA 2
     (64, 2, 2, 66, 5),     # chunks of 33 tokens
     (128, 2, 2, 2, 4),     # one token per chunk
-    # group 3 (not a divisor of the wave count), chunks of 32.  (With head_dim 128 and
-    # chunks of 64 this seed puts |dV| = 5 on key 1, where the bf16 rounding of P alone --
-    # emulated in fp64 -- already costs 1.13e-2, the kernel's exact error; this shape's
-    # floor is 7.6e-3.)
-    (64, 6, 2, 64, 4),
+    (64, 6, 2, 64, 4),     # group 3 (not a divisor of the wave count), chunks of 32
+    (128, 4, 1, 200, 3),   # GQA 4 over 600 tokens: |dV| 6.5 on key 0
+    (128, 2, 1, 2, 4),     # one token per chunk, shared K/V head: few dQ terms
+    (128, 6, 2, 128, 4),   # group 3, head_dim 128, chunks of 64: |dV| 7.3
 ]
 
 

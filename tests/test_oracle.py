@@ -345,6 +345,45 @@ def test_backward_single_key_has_zero_dq():
     np.testing.assert_allclose(dv[0], do.sum(axis=0), atol=1e-14)
 
 
+@pytest.mark.parametrize("causal,hq,hkv", [(False, 2, 2), (True, 4, 2), (True, 3, 1)])
+def test_backward_at_chosen_keys_equals_full_backward(causal, hq, hkv):
+    """attention_bwd_keys (dK/dV at a few keys, over every row) agrees with the columns
+    of the full analytic backward, which finite differences pin; causal keys include
+    key 0 (seen by every row) and the last key (seen by one row)."""
+    n, d = 70, 16
+    q, k, v = qkv(41, n, n, hq, hkv, d)
+    do = rand(42, (n, hq, d))
+    _, dk, dv, _, _ = oracle.attention_bwd(q, k, v, do, causal=causal)
+    keys = np.array([0, 1, 33, 34, 68, 69])
+    dk_s, dv_s = oracle.attention_bwd_keys(q, k, v, do, causal=causal, keys=keys)
+    np.testing.assert_allclose(dk_s, dk[keys], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(dv_s, dv[keys], atol=1e-12, rtol=0)
+
+
+def test_backward_at_chosen_keys_finite_differences():
+    """dK/dV at chosen keys against central differences of L = sum(O * dO) with respect
+    to those keys' rows alone (causal, grouped heads)."""
+    n, hq, hkv, d = 40, 2, 1, 32
+    q, k, v = qkv(43, n, n, hq, hkv, d)
+    do = rand(44, (n, hq, d))
+    keys = np.array([0, 19, 39])
+    dk_s, dv_s = oracle.attention_bwd_keys(q, k, v, do, causal=True, keys=keys)
+    rng = np.random.default_rng(45)
+    h = 1e-6
+    for name, x, g in (("k", k, dk_s), ("v", v, dv_s)):
+        for _ in range(3):
+            u = np.zeros_like(x)
+            u[keys] = rng.standard_normal((keys.size,) + x.shape[1:])
+            args = {"q": q, "k": k, "v": v}
+            args[name] = x + h * u
+            lp = _loss(args["q"], args["k"], args["v"], do, True)
+            args[name] = x - h * u
+            lm = _loss(args["q"], args["k"], args["v"], do, True)
+            fd = (lp - lm) / (2 * h)
+            an = float(np.sum(g * u[keys]))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
 # ------------------------------------------------------------ zig-zag layout
 @pytest.mark.parametrize("D", [1, 2, 4, 8])
 def test_zigzag_positions_partition_the_sequence(D):
