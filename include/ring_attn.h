@@ -291,6 +291,29 @@ int ring_attn_decode(const void* q, const void* const* k_blocks, const void* con
                      long long q_pos0, float* out, float* lse, ra_stream_t stream);
 
 /*
+ * ring_attn_decode_noalloc -- ring_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, layouts, results and
+ * errors as ring_attn_decode (it runs the same kernels), but the split-key
+ * partials go to a fixed device array compiled into the library,
+ * RA_DECODE_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends,
+ * instead of a lazily grown buffer; the call performs no allocation and
+ * creates no library stream or event.  A shape whose partials need more than
+ * that (about kv_heads * partials * rows * (head_dim + 1) floats; the 512k
+ * GQA 32/8 workload with 4 query rows needs 8.5 MB) returns
+ * RA_ERR_INVALID_ARG and enqueues nothing.  Every such call on one GPU shares
+ * the array, which keeps the last call's contents: calls that overlap in time
+ * on one GPU (different streams) race on it and must be serialised by the
+ * caller; unlike the other entry points this one is not ordered against
+ * other library calls.
+ */
+#define RA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ring_attn_decode_noalloc(const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                             int n_blocks, int block_len, int q_len, int heads, int kv_heads,
+                             int head_dim, long long q_pos0, float* out, float* lse,
+                             ra_stream_t stream);
+
+/*
  * ring_attn_ffn_blockwise -- the feedforward half of a blockwise transformer
  * layer, computed block by block ("Ring Attention with Blockwise Transformers
  * for Near-Infinite Context" close-reading notes, §2.2: computing the

@@ -30,7 +30,7 @@ EXPORTED = (
     "ring_attn_last_error", "ring_attn_workspace_bytes", "ring_attn_profile_enable",
     "ring_attn_profile_read", "ring_attn_shutdown", "ring_attn_schedule", "ring_attn_debug",
     "ring_attn_set_workspace", "ring_attn_mfma_rate", "ring_attn_decode",
-    "ring_attn_fwd_zigzag", "ring_attn_bwd_zigzag", "ring_attn_ffn_blockwise",
+    "ring_attn_fwd_zigzag", "ring_attn_bwd_zigzag", "ring_attn_ffn_blockwise", "ring_attn_decode_noalloc",
 )
 MFMA_RATE_SINK_FLOATS = 1024
 
@@ -72,8 +72,10 @@ def lib() -> ctypes.CDLL:
     L.ring_attn_workspace_bytes.restype = ctypes.c_size_t
     L.ring_attn_set_workspace.argtypes = [vp, ctypes.c_size_t]
     L.ring_attn_set_workspace.restype = i
-    L.ring_attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_longlong, vp, vp, vp]
-    L.ring_attn_decode.restype = i
+    for name in ("ring_attn_decode", "ring_attn_decode_noalloc"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_longlong, vp, vp, vp]
+        fn.restype = i
     L.ring_attn_ffn_blockwise.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, vp]
     L.ring_attn_ffn_blockwise.restype = i
     L.ring_attn_mfma_rate.argtypes = [i, vp, ctypes.POINTER(ctypes.c_double), vp]
@@ -201,6 +203,14 @@ def ring_attn_decode(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, k
                      lse, stream=None) -> int:
     return lib().ring_attn_decode(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks, block_len, q_len,
                                   heads, kv_heads, head_dim, int(q_pos0), _addr(out), _addr(lse), _stream(stream))
+
+
+def ring_attn_decode_noalloc(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0,
+                             out, lse, stream=None) -> int:
+    """ring_attn_decode with its partials in the library's fixed device scratch (allocates nothing)."""
+    return lib().ring_attn_decode_noalloc(_addr(q), _ptr_array(k_blocks), _ptr_array(v_blocks), n_blocks, block_len,
+                                          q_len, heads, kv_heads, head_dim, int(q_pos0), _addr(out), _addr(lse),
+                                          _stream(stream))
 
 
 def ring_attn_ffn_blockwise(x, w1, b1, w2, b2, rows, hidden, ffn, chunk_rows, y, stream=None) -> int:

@@ -19,6 +19,11 @@
 // a normalised partial (o, lse) per row.
 // Kernel 2 (decode_merge_kernel): one workgroup per (K/V head, row) folds the
 // partials of all chunks and blocks with the log-sum-exp merge.
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/ring_attn.h"
 #include "kcommon.h"
 #include "kernels.h"
 
@@ -256,6 +261,38 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fixed scratch
+// The partials of the entry point that allocates nothing live in this
+// file-scope device array: one copy per GPU, held until the process ends,
+// shared by every such call on that GPU.  In host code the name `scratch` is
+// only a stand-in for the symbol (passing it to a kernel would hand the GPU a
+// host address); its device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and only that address is used.
+constexpr size_t kDecodeScratchBytes = RA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(float** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, float*>> addr;  // (device, address of its copy)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& da : addr)
+    if (da.first == dev) {
+      *ptr = da.second;
+      *bytes = kDecodeScratchBytes;
+      return hipSuccess;
+    }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  addr.emplace_back(dev, static_cast<float*>(p));
+  *ptr = static_cast<float*>(p);
+  *bytes = kDecodeScratchBytes;
+  return hipSuccess;
 }
 
 }  // namespace ra

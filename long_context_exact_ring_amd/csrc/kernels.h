@@ -127,6 +127,9 @@ hipError_t launch_gemm_bt(const GemmArgs& a, bool gelu_bf16_out, hipStream_t st)
 int gemm_tile_n();
 int gemm_tile_k();
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
+// Device address and size of the fixed decode scratch on the current device (the
+// partials of the no-allocation entry point); looked up once per device.
+hipError_t decode_scratch(float** ptr, size_t* bytes);
 
 // Pipeline diagnostics: NaN-fill two staging buffers; spin for a bounded number of cycles.
 hipError_t launch_fill_nan(void* a, void* b, size_t bytes, hipStream_t st);

@@ -188,7 +188,7 @@ struct CallOrder {
     return RA_OK;
   }
   ~CallOrder() {
-    if (hipEventRecord(c->ev_last, st) == hipSuccess) c->last_valid = true;
+    if (c && hipEventRecord(c->ev_last, st) == hipSuccess) c->last_valid = true;
   }
 };
 
@@ -776,9 +776,13 @@ int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
 #define RA_DEC_WAVES 1024
 #endif
 
+// noalloc: the partials go to the library's fixed device array (decode_scratch)
+// instead of the lazily grown per-device buffer; nothing is allocated, no
+// library stream or event is created, and the call is not ordered against
+// other calls (callers that overlap such calls on one GPU race on the array).
 int decode_impl(const void* q, const void* const* kb, const void* const* vb, int n_blocks, int block_len,
                 int q_len, int heads, int kv_heads, int head_dim, long long q_pos0, float* out, float* lse,
-                hipStream_t stream) {
+                hipStream_t stream, bool noalloc) {
   if (!q || !out || !lse) return fail(RA_ERR_INVALID_ARG, "q, out and lse must be non-NULL");
   if (!kb || !vb) return fail(RA_ERR_INVALID_ARG, "k_blocks/v_blocks array is NULL");
   if (n_blocks < 1 || n_blocks > kDecodeMaxBlocks)
@@ -821,12 +825,24 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   const size_t need = (size_t)kv_heads * n_parts * rows * (head_dim + 1) * sizeof(float);
 
   std::lock_guard<std::mutex> lk(g_mu);
-  Ctx* c = nullptr;
-  int st = get_ctx(&c);
-  if (st != RA_OK) return st;
-  CallOrder order(c, stream);
-  if ((st = order.begin()) != RA_OK) return st;
-  if ((st = ensure_dec(c, need)) != RA_OK) return st;
+  float* part = nullptr;
+  CallOrder order(nullptr, stream);  // ordered against other calls unless noalloc
+  if (noalloc) {
+    size_t cap = 0;
+    RA_HIP(decode_scratch(&part, &cap));
+    if (need > cap)
+      return fail(RA_ERR_INVALID_ARG,
+                  "decode partials need %zu bytes; the fixed scratch of the no-allocation entry point holds %zu",
+                  need, cap);
+  } else {
+    Ctx* c = nullptr;
+    int st = get_ctx(&c);
+    if (st != RA_OK) return st;
+    order.c = c;
+    if ((st = order.begin()) != RA_OK) return st;
+    if ((st = ensure_dec(c, need)) != RA_OK) return st;
+    part = c->dec;
+  }
   DecodeArgs a{};
   a.q = q;
   for (int j = 0; j < n_blocks; ++j) {
@@ -835,8 +851,8 @@ int decode_impl(const void* q, const void* const* kb, const void* const* vb, int
   }
   a.out = out;
   a.lse = lse;
-  a.part_o = c->dec;
-  a.part_lse = c->dec + (size_t)kv_heads * n_parts * rows * head_dim;
+  a.part_o = part;
+  a.part_lse = part + (size_t)kv_heads * n_parts * rows * head_dim;
   a.q_pos0 = q_pos0;
   a.n_blocks = n_blocks;
   a.len = block_len;
@@ -1101,7 +1117,15 @@ int ring_attn_decode(const void* q, const void* const* k_blocks, const void* con
                      float* lse, ra_stream_t stream) {
   ra::clear_error();
   return ra::decode_impl(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0, out,
-                         lse, (hipStream_t)stream);
+                         lse, (hipStream_t)stream, false);
+}
+
+int ring_attn_decode_noalloc(const void* q, const void* const* k_blocks, const void* const* v_blocks, int n_blocks,
+                             int block_len, int q_len, int heads, int kv_heads, int head_dim, long long q_pos0,
+                             float* out, float* lse, ra_stream_t stream) {
+  ra::clear_error();
+  return ra::decode_impl(q, k_blocks, v_blocks, n_blocks, block_len, q_len, heads, kv_heads, head_dim, q_pos0, out,
+                         lse, (hipStream_t)stream, true);
 }
 
 int ring_attn_ffn_blockwise(const void* x, const void* w1, const float* b1, const void* w2, const float* b2, int rows,
