@@ -742,9 +742,10 @@ int profile_read(double* ms, int* count, double* copy_ms, double* hidden_ms) {
     }
     for (auto& cp : copy) {
       cms += cp.b - cp.a;
-      // overlap of this copy with the union of kernel intervals
+      // overlap of this copy with the union of the kernel intervals of the same call
       std::vector<std::pair<double, double>> cut;
       for (auto& k : kern) {
+        if (k.call != cp.call) continue;
         const double lo = std::max(cp.a, k.a), hi = std::min(cp.b, k.b);
         if (hi > lo) cut.push_back({lo, hi});
       }
