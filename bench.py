@@ -58,10 +58,11 @@ def parse():
                         "rocprofv3 --pmc pass of SQ counters")
     p.add_argument("--summarize-overlap", nargs=2, metavar=("KERNEL_TRACE_CSV", "MEMORY_COPY_TRACE_CSV"),
                    help="no GPU work: share of the device-to-device copy time hidden under kernels")
-    p.add_argument("--summarize-gaps", metavar="KERNEL_TRACE_CSV",
-                   help="no GPU work: idle time of the compute stream between consecutive kernels of the timed "
-                        "steps of a rocprofv3 --kernel-trace run of this bench (same --steps/--warmup), i.e. an "
-                        "upper bound on the exposed K/V rotation copy time")
+    p.add_argument("--summarize-gaps", nargs="+", metavar="CSV_OR_JSON",
+                   help="no GPU work: KERNEL_TRACE_CSV [BENCH_JSON]: idle time of the compute stream between "
+                        "consecutive kernels of the timed steps of a rocprofv3 --kernel-trace run of this bench (same "
+                        "--steps/--warmup), an upper bound on the exposed K/V rotation copy time; with the JSON line "
+                        "that run printed, a lower bound on the hidden fraction of its copies")
     p.add_argument("--sweep-block-len", action="store_true",
                    help="the overlap condition of the ring: for block lengths 1024..16384 (32 heads x 128, "
                         "non-causal, one rank against 8 blocks) measure per-round kernel time, copy time and "
@@ -542,7 +543,7 @@ def summarize_overlap(kernel_trace_csv: str, copy_trace_csv: str):
     return hidden / max(total, 1)
 
 
-def summarize_gaps(trace_csv: str, steps: int, warmup: int, copy_ms_per_step=None):
+def summarize_gaps(trace_csv: str, steps: int, warmup: int, bench_json: str | None = None):
     """Idle time of the compute stream inside the timed steps of a kernel-trace run.
 
     Every kernel of a ring step runs on the caller's stream; the K/V copies run on
@@ -550,7 +551,12 @@ def summarize_gaps(trace_csv: str, steps: int, warmup: int, copy_ms_per_step=Non
     So the gaps between consecutive kernels (launch latency included) bound the
     exposed copy time from above.  The bench's kernels are the same in every step:
     the timed steps are the last steps/(warmup+steps) of the kernels before the
-    matrix-core rate probe that follows the timed region."""
+    matrix-core rate probe that follows the timed region.  Gaps are also listed
+    by the pair of kernels around them: a dK/dV -> dQ gap never waits for a copy
+    (the same round), so it gives the launch-to-launch baseline.  With the JSON
+    line the traced bench printed, the copy time of that same run (library
+    events) turns the idle time into a lower bound on the hidden fraction."""
+    import collections
     import csv
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
     names = [r["Kernel_Name"] for r in rows]
@@ -561,16 +567,35 @@ def summarize_gaps(trace_csv: str, steps: int, warmup: int, copy_ms_per_step=Non
         sys.exit(f"{len(ring)} kernels do not split into {steps + warmup} equal steps")
     per = len(ring) // (steps + warmup)
     timed = ring[-steps * per:]
-    gaps = [max(0, int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) for a, b in zip(timed, timed[1:])]
+
+    def kind(name):
+        for k in ("fwd_bf16", "fwd_step", "bwd_dkdv", "bwd_dq", "bwd_pre", "FillFunctor"):
+            if k in name:
+                return k
+        return name[:40]
+
+    gaps, by_pair = [], collections.defaultdict(list)
+    for a, b in zip(timed, timed[1:]):
+        g = max(0, int(b["Start_Timestamp"]) - int(a["End_Timestamp"]))
+        gaps.append(g)
+        by_pair[(kind(a["Kernel_Name"]), kind(b["Kernel_Name"]))].append(g)
     busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in timed)
     span = int(timed[-1]["End_Timestamp"]) - int(timed[0]["Start_Timestamp"])
     gap_ms = sum(gaps) / 1e6 / steps
     out = {"kernels_per_step": per, "span_ms_per_step": span / 1e6 / steps, "kernel_ms_per_step": busy / 1e6 / steps,
-           "idle_ms_per_step": gap_ms, "largest_gap_us": max(gaps) / 1e3 if gaps else 0.0,
-           "gaps_over_20us": sum(1 for g in gaps if g > 20000) / steps}
-    if copy_ms_per_step:
-        out["copy_ms_per_step"] = copy_ms_per_step
-        out["hidden_frac_lower_bound"] = max(0.0, 1.0 - gap_ms / copy_ms_per_step)
+           "idle_ms_per_step": gap_ms, "largest_gap_us": max(gaps) / 1e3 if gaps else 0.0}
+    if bench_json:
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        cms = rec["overlap"]["copy_ms_per_step"]
+        out["copy_ms_per_step_same_run"] = cms
+        out["copy_ms_per_launch_same_run"] = rec["kernels"]["copy"]["avg_launch_ms"]
+        out["hidden_frac_lower_bound"] = max(0.0, 1.0 - gap_ms / cms)
+    print("| previous kernel -> next kernel | gaps per step | idle (ms per step) | median gap (us) | max gap (us) |")
+    print("|---|---|---|---|---|")
+    for pair, gs in sorted(by_pair.items(), key=lambda kv: -sum(kv[1])):
+        gs = sorted(gs)
+        print(f"| {pair[0]} -> {pair[1]} | {len(gs) // steps} | {sum(gs) / 1e6 / steps:.1f} | "
+              f"{gs[len(gs) // 2] / 1e3:.1f} | {gs[-1] / 1e3:.1f} |")
     print(json.dumps(out))
     return out
 
@@ -648,7 +673,8 @@ def main():
         summarize_overlap(*args.summarize_overlap)
         return
     if args.summarize_gaps:
-        summarize_gaps(args.summarize_gaps, args.steps, args.warmup)
+        summarize_gaps(args.summarize_gaps[0], args.steps, args.warmup,
+                       args.summarize_gaps[1] if len(args.summarize_gaps) > 1 else None)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not built "
