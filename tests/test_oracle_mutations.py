@@ -115,3 +115,56 @@ def test_backward_mutation_dropped_delta_is_caught(monkeypatch):
     finally:
         monkeypatch.undo()
     assert err > 1e-4
+
+
+def pins_keys_error():
+    """dK/dV at chosen keys (attention_bwd_keys) against central differences of the dense forward."""
+    n, d = 12, 4
+    q, k, v = rand(5, (n, 2, d), 1, 0), rand(5, (n, 1, d), 1, 1), rand(5, (n, 1, d), 1, 2)
+    do = rand(6, (n, 2, d))
+    keys = np.array([0, 5, 11])
+    dk, dv = oracle.attention_bwd_keys(q, k, v, do, causal=True, keys=keys)
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for name, x, g in (("k", k, dk), ("v", v, dv)):
+        u = np.zeros_like(x)
+        u[keys] = rng.standard_normal((keys.size,) + x.shape[1:])
+        a = {"q": q, "k": k, "v": v}
+        a[name] = x + 1e-6 * u
+        lp = np.sum(oracle.attention_fwd(a["q"], a["k"], a["v"], causal=True)[0] * do)
+        a[name] = x - 1e-6 * u
+        lm = np.sum(oracle.attention_fwd(a["q"], a["k"], a["v"], causal=True)[0] * do)
+        worst = max(worst, abs((lp - lm) / 2e-6 - np.sum(g * u[keys])))
+    return worst
+
+
+def test_chosen_key_backward_pins_pass_unmutated():
+    assert pins_keys_error() < 1e-6
+
+
+def test_chosen_key_backward_mutations_are_caught(monkeypatch):
+    # a causal mask shifted by one key in the chosen-key scores only (the forward, which the
+    # finite differences differentiate, keeps the right mask; the 3-key calls are the chosen keys)
+    def mask_off_by_one_at_chosen_keys(qh, kg, scale, causal, q_pos, k_pos):
+        if kg.shape[0] == 3:
+            return _ORIG_SCORES(qh, kg, scale, causal, q_pos - 1, k_pos)
+        return _ORIG_SCORES(qh, kg, scale, causal, q_pos, k_pos)
+
+    monkeypatch.setattr(dense, "_scores", mask_off_by_one_at_chosen_keys)
+    assert pins_keys_error() > 1e-4
+    monkeypatch.undo()
+    # dS without Delta: the row term of the chosen-key backward dropped
+    orig_sum = np.sum
+
+    def zero_delta(a, axis=None, **kw):
+        r = orig_sum(a, axis=axis, **kw)
+        if axis == 1 and getattr(a, "ndim", 0) == 2:
+            return np.zeros_like(r)
+        return r
+
+    monkeypatch.setattr(dense.np, "sum", zero_delta)
+    try:
+        err = pins_keys_error()
+    finally:
+        monkeypatch.undo()
+    assert err > 1e-4
