@@ -40,23 +40,30 @@ def sample_rows(c, n_random=12, seed=0):
     return np.unique(np.concatenate([fixed, rng.integers(0, c, n_random)]).astype(np.int64))
 
 
-def check_fwd_sampled(w, rank, out, lse, kblk, vblk, heads):
+def check_fwd_rows_all_heads(w, rank, out, lse, kblk, vblk, rows):
+    """Every head of the chosen rows of one rank against the oracle, one oracle call per head
+    (side by side on the host's cores)."""
     c = w.block_len
     group = w.heads // w.kv_heads
-    kvh = [h // group for h in heads]
-    q = gen_block(w.seed, "q", rank, c, w.heads, w.head_dim, w.dtype)
-    rows = sample_rows(c, seed=rank)
+    q = gen_block(w.seed, "q", rank, c, w.heads, w.head_dim, w.dtype)[rows]
     nvis = rank + 1 if w.causal else w.n_blocks
-    k = np.concatenate([kb[:, kvh] for kb in kblk[:nvis]])
-    v = np.concatenate([vb[:, kvh] for vb in vblk[:nvis]])
-    o_ref, l_ref = oracle.sampled_rows_fwd(q[rows][:, heads], rank * c + rows, k, v, causal=w.causal)
-    o = out[torch.from_numpy(rows).cuda()][:, heads]
-    l = lse[heads][:, torch.from_numpy(rows).cuda()]
-    compare(f"{w.name} rank {rank} out", o, o_ref, w.dtype)
-    compare(f"{w.name} rank {rank} lse", l, l_ref, w.dtype)
+    k_all = np.concatenate(kblk[:nvis])
+    v_all = np.concatenate(vblk[:nvis])
+
+    def ref(h):
+        g = h // group
+        return oracle.sampled_rows_fwd(q[:, [h]], rank * c + rows, k_all[:, [g]], v_all[:, [g]], causal=w.causal)
+
+    refs = _pool(ref, list(range(w.heads)))
+    o_ref = np.concatenate([r[0] for r in refs], axis=1)
+    l_ref = np.concatenate([r[1] for r in refs], axis=0)
+    idx = torch.from_numpy(rows).cuda()
+    compare(f"{w.name} rank {rank} out ({rows.size} rows x {w.heads} heads)", out[idx], o_ref, w.dtype)
+    compare(f"{w.name} rank {rank} lse", lse[:, idx], l_ref, w.dtype)
 
 
 def test_full_noncausal_64k_h16_d64():
+    """Every head at the first and last 64 rows and every 64th row of the query block."""
     require_gpu()
     w = WORKLOADS["noncausal_64k_h16_d64"]
     log(f"workload {w.name}")
@@ -66,7 +73,9 @@ def test_full_noncausal_64k_h16_d64():
     q = up(gen_block(w.seed, "q", 0, w.block_len, w.heads, w.head_dim, w.dtype), w.dtype)
     out, lse = ra.fwd(q, kb, vb, causal=False, rank=0)
     torch.cuda.synchronize()
-    check_fwd_sampled(w, 0, out, lse, kblk, vblk, heads=list(range(w.heads)))
+    c = w.block_len
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(c - 64, c), np.arange(0, c, 64)])).astype(np.int64)
+    check_fwd_rows_all_heads(w, 0, out, lse, kblk, vblk, rows)
 
 
 def dense_rows(c):
@@ -196,7 +205,10 @@ def test_full_causal_512k_gqa_rank7():
     q = up(gen_block(w.seed, "q", 7, w.block_len, w.heads, w.head_dim, w.dtype), w.dtype)
     out, lse = ra.fwd(q, kb, vb, causal=True, rank=7)
     torch.cuda.synchronize()
-    check_fwd_sampled(w, 7, out, lse, kblk, vblk, heads=[0, 5, 31])
+    # every head at the first and last 64 rows and every 512th row (each sees up to all 524288 keys)
+    c = w.block_len
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(c - 64, c), np.arange(0, c, 512)])).astype(np.int64)
+    check_fwd_rows_all_heads(w, 7, out, lse, kblk, vblk, rows)
 
 
 def test_full_backward_causal_32k():
