@@ -267,3 +267,73 @@ def test_full_causal_128k_zigzag_sampled():
         o_ref, l_ref = oracle.sampled_rows_fwd(q[rows][:, heads], qpos, k, v, causal=True, k_pos=kpos[order])
         compare(f"zigzag rank {r} out", out[torch.from_numpy(rows).cuda()][:, heads], o_ref, w.dtype)
         compare(f"zigzag rank {r} lse", lse[heads][:, torch.from_numpy(rows).cuda()], l_ref, w.dtype)
+
+
+def test_full_backward_causal_128k_zigzag():
+    """The zig-zag layout's backward at full size, as its bench workload runs it (forward and
+    backward of every rank, dK/dV accumulated over the ranks).  dQ: sampled rows of every rank,
+    every head.  dK/dV: heads 0 and 31 at keys of both chunks of blocks 0, 7 and 15, against the
+    oracle over all 131072 rows at their zig-zag positions."""
+    require_gpu()
+    w = WORKLOADS["causal_128k_h32_d128_zigzag"]
+    log(f"workload {w.name} backward")
+    t0 = time.time()
+    c, D, H, d = w.block_len, w.n_blocks, w.heads, w.head_dim
+    kblk, vblk = kv_blocks(w)
+    kb = [up(x, w.dtype) for x in kblk]
+    vb = [up(x, w.dtype) for x in vblk]
+    qs = [gen_block(w.seed, "q", r, c, H, d, w.dtype) for r in range(D)]
+    dos = [gen_block(w.seed, "do", r, c, H, d, w.dtype) for r in range(D)]
+    dkb = [torch.zeros((c, w.kv_heads, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+    dvb = [torch.zeros((c, w.kv_heads, d), dtype=torch.float32, device="cuda") for _ in range(D)]
+    qrows = {r: sample_rows(c, n_random=4, seed=200 + r) for r in range(D)}
+    dq_got = {}
+    for r in range(D):
+        qd, dod = up(qs[r], w.dtype), up(dos[r], w.dtype)
+        o, l = ra.fwd(qd, kb, vb, causal=True, rank=r, zigzag=True)
+        g, _, _ = ra.bwd(qd, kb, vb, o, dod, l, causal=True, rank=r, dk_blocks=dkb, dv_blocks=dvb, zigzag=True)
+        dq_got[r] = g[torch.from_numpy(qrows[r]).cuda()].cpu()
+    torch.cuda.synchronize()
+
+    # the whole sequence in position order: block b's rows sit at zigzag_positions(b)
+    pos = np.concatenate([oracle.zigzag_positions(j, D, c) for j in range(D)])
+    order = np.argsort(pos)  # order[p] = row (in block-concatenated order) at position p
+    k_pos = np.arange(D * c, dtype=np.int64)
+    k_all = np.concatenate(kblk)[order]
+    v_all = np.concatenate(vblk)[order]
+
+    def dq_ref(r):
+        rows = qrows[r]
+        g, _, _, _, _ = oracle.attention_bwd(qs[r][rows], k_all, v_all, dos[r][rows], causal=True,
+                                             q_pos=oracle.zigzag_positions(r, D, c)[rows], k_pos=k_pos)
+        return g
+
+    for r, ref in zip(range(D), _pool(dq_ref, list(range(D)))):
+        compare(f"zigzag dq rank {r} ({qrows[r].size} rows x {H} heads)", dq_got[r], ref, w.dtype)
+
+    heads = [0, 31]
+    h2 = c // 2
+    kidx = np.array([b * c + t for b in (0, 7, 15) for t in (0, 1, h2 - 1, h2, h2 + 1, c - 1)], dtype=np.int64)
+    dk_got = torch.cat(dkb, 0)[torch.from_numpy(kidx).cuda()][:, heads].cpu()
+    dv_got = torch.cat(dvb, 0)[torch.from_numpy(kidx).cuda()][:, heads].cpu()
+    keys = pos[kidx]  # the chosen keys' positions = their indices in position order
+    q_h = np.concatenate(qs)[order][:, heads]
+    do_h = np.concatenate(dos)[order][:, heads]
+    k_h, v_h = k_all[:, heads], v_all[:, heads]
+    step = 8192
+
+    def dkdv_part(task):  # one row range (in position order) of one head
+        r0, i = task
+        r1 = min(D * c, r0 + step)
+        return oracle.attention_bwd_keys(q_h[r0:r1, [i]], k_h[:, [i]], v_h[:, [i]], do_h[r0:r1, [i]], causal=True,
+                                         keys=keys, q_pos=np.arange(r0, r1), k_pos=k_pos)
+
+    tasks = [(r0, i) for r0 in reversed(range(0, D * c, step)) for i in range(len(heads))]  # longest first
+    parts = dict(zip(tasks, _pool(dkdv_part, tasks)))
+    dk_ref = np.concatenate([np.sum([parts[(r0, i)][0] for r0 in range(0, D * c, step)], axis=0)
+                             for i in range(len(heads))], axis=1)
+    dv_ref = np.concatenate([np.sum([parts[(r0, i)][1] for r0 in range(0, D * c, step)], axis=0)
+                             for i in range(len(heads))], axis=1)
+    compare(f"zigzag dk heads {heads} at {keys.size} keys", dk_got, dk_ref, w.dtype)
+    compare(f"zigzag dv heads {heads} at {keys.size} keys", dv_got, dv_ref, w.dtype)
+    log(f"  {time.time() - t0:.1f}s")
