@@ -173,8 +173,12 @@ int ring_attn_bwd_f32(const float* q, const float* const* k_blocks, const float*
  * rank then owns the same amount of work (each ring round pairs one early
  * and one late chunk), instead of rank r doing r + 1 rounds of the
  * contiguous layout; the ring visits every block in every rank.  Chunk pairs
- * are processed as half-size steps: a key chunk later than the query chunk is
- * skipped, the same chunk is the masked diagonal, an earlier one is full.
+ * are the units of work: a key chunk later than the query chunk is skipped,
+ * the same chunk is the masked diagonal, an earlier one is full.  Where one
+ * query chunk sees both key chunks of a block off the diagonal (for dK/dV:
+ * one key chunk is seen by both query chunks), the two pairs run as one step
+ * over the whole block, so a round is never split into more kernel steps than
+ * its diagonal requires.
  * Arguments, layouts, ownership and errors are those of ring_attn_fwd and
  * ring_attn_bwd (bf16), except that block_len must be even
  * (RA_ERR_INVALID_ARG otherwise) and row i of every per-block tensor sits at

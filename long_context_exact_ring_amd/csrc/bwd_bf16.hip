@@ -73,7 +73,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int KW = NW * 32;
-  const int nkt = (a.len + KW - 1) / KW;
+  const int nkt = (a.klen + KW - 1) / KW;
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   const int kt = logical % nkt;  // ascending: with a causal diagonal, low key tiles are heaviest
   const int g = logical / nkt;
@@ -88,17 +88,17 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
   // lane's V row is loaded and converted in registers (B operands with keys
   // on lanes) and written out too.  The half copies feed the dQ kernel of the
   // same round: every key of every K/V head belongs to exactly one workgroup.
-  dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.len,
+  dma_rows<D, NW * 32, NW>(reinterpret_cast<const bf16_storage*>(a.k) + (size_t)g * D, kvstride, kb0, a.klen,
                            ktile, wu, lane);
   Frag<bf16_storage> vf[D / 16];
   {
-    const int kr = min(key, a.len - 1);  // lanes past the end compute garbage that is never stored
+    const int kr = min(key, a.klen - 1);  // lanes past the end compute garbage that is never stored
     const size_t off = (size_t)kr * kvstride + (size_t)g * D + hf * 8;
     const bf16_storage* vp = reinterpret_cast<const bf16_storage*>(a.v) + off;
     bf16_storage* v16 = reinterpret_cast<bf16_storage*>(a.v16) + off;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) vf[ks].v = bf16x8_to_f16x8(ld16(vp + ks * 16));
-    if (key < a.len)
+    if (key < a.klen)
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) st16(v16 + ks * 16, vf[ks].v);
   }
@@ -112,7 +112,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
       uint4* p = reinterpret_cast<uint4*>(ktile + r * ROWB + slot * 16);
       const uint4 kh = bf16x8_to_f16x8(*p);
       *p = kh;
-      if (kb0 + r < a.len) st16(k16 + (size_t)(kb0 + r) * kvstride + ((slot ^ swz<D>(r)) * 8), kh);
+      if (kb0 + r < a.klen) st16(k16 + (size_t)(kb0 + r) * kvstride + ((slot ^ swz<D>(r)) * 8), kh);
     }
   }
   __syncthreads();  // the half K rows are in LDS
@@ -239,7 +239,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a) {
     for (; it < base + nqt; ++it) step(it, std::true_type{});
   }
 
-  if (key >= a.len) return;
+  if (key >= a.klen) return;
   float* dkp = a.dk + (size_t)key * kvstride + (size_t)g * D;
   float* dvp = a.dv + (size_t)key * kvstride + (size_t)g * D;
 #pragma unroll
@@ -301,9 +301,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
   const int qi = row0 + n;
   const int wg_first_row = rt * R;
   const int wg_last_row = min(rt * R + R, a.len) - 1;
-  int ntiles = (a.len + BC - 1) / BC;
+  int ntiles = (a.klen + BC - 1) / BC;
   if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
-  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
+  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.klen / BC);
 
   const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
   Frag<bf16_storage> qf[D / 16], of[D / 16];
@@ -338,7 +338,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
     goff[j] = (uint32_t)(r * kvstride + (slot ^ swz<D>(r)) * 8) * 2;
   }
   auto issue = [&](int t, unsigned char* st) {
-    if ((t + 1) * BC <= a.len) {
+    if ((t + 1) * BC <= a.klen) {
       const size_t tb = (size_t)t * BC * kvstride * 2;
       const unsigned char* kb = reinterpret_cast<const unsigned char*>(kbase) + tb;
       const unsigned char* vb = reinterpret_cast<const unsigned char*>(vbase) + tb;
@@ -350,8 +350,8 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
         lds_dma16_off(vb, goff[j], __builtin_amdgcn_readfirstlane(lds_addr(st + TILEB + q * 1024)));
       }
     } else {
-      dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.len, st, wu, lane);
-      dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.len, st + TILEB, wu, lane);
+      dma_rows<D, BC, NW>(kbase, kvstride, t * BC, a.klen, st, wu, lane);
+      dma_rows<D, BC, NW>(vbase, kvstride, t * BC, a.klen, st + TILEB, wu, lane);
     }
   };
   const LdsOperandOffsets<D> lo(lane, 0);  // row reads of K and V, transposed reads of K
@@ -373,7 +373,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a) {
         mma_h(dp[kt], vf, of[ks]);
       }
     }
-    const int lim = (a.diag ? min(qi, a.len - 1) : a.len - 1) - t0;  // visible local keys: <= lim
+    const int lim = (a.diag ? min(qi, a.klen - 1) : a.klen - 1) - t0;  // visible local keys: <= lim
 #pragma unroll
     for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_pair_kernel(ArgPair<BwdAr
 template <int D>
 static hipError_t launch_dkdv_bf16_t(const BwdArgs* a, int nsub, hipStream_t st) {
   const int KW = kKvNW * 32;
-  const int nblk = ((a[0].len + KW - 1) / KW) * a[0].hkv;
+  const int nblk = ((a[0].klen + KW - 1) / KW) * a[0].hkv;
   if (nblk == 0) return hipSuccess;
   ArgPair<BwdArgs> pair{};
   for (int i = 0; i < nsub; ++i) pair.s[i] = a[i];

@@ -353,11 +353,12 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// sub-problems of one launch must agree on the grid: same length and head layout
+// sub-problems of one launch must agree on the grid: same lengths and head layout.
+// A causal diagonal block pairs query row i with key i, so it needs as many keys as rows.
 static bool same_bwd_grid(const BwdArgs* a, int nsub) {
-  for (int i = 1; i < nsub; ++i)
-    if (a[i].len != a[0].len || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv || a[i].hpw != a[0].hpw ||
-        a[i].hsub != a[0].hsub)
+  for (int i = 0; i < nsub; ++i)
+    if (a[i].len != a[0].len || a[i].klen != a[0].klen || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv ||
+        a[i].hpw != a[0].hpw || a[i].hsub != a[0].hsub || (a[i].diag && a[i].klen != a[i].len))
       return false;
   return true;
 }
@@ -365,7 +366,8 @@ static bool same_bwd_grid(const BwdArgs* a, int nsub) {
 hipError_t launch_bwd_dkdv(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
   if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
   if (elem_bytes == 2) return launch_bwd_dkdv_bf16(ap, nsub, head_dim, st);
-  if (nsub != 1 || elem_bytes != 4) return hipErrorInvalidValue;  // fp32: one sub-problem per launch
+  // fp32: one sub-problem per launch, as many keys as query rows
+  if (nsub != 1 || elem_bytes != 4 || ap[0].klen != ap[0].len) return hipErrorInvalidValue;
   const BwdArgs& a = ap[0];
   if (head_dim == 64) return launch_dkdv_t<float, 64, 32>(a, st);
   if (head_dim == 128) return launch_dkdv_t<float, 128, 32>(a, st);
@@ -375,7 +377,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs* ap, int nsub, int elem_bytes, int head
 hipError_t launch_bwd_dq(const BwdArgs* ap, int nsub, int elem_bytes, int head_dim, hipStream_t st) {
   if (nsub < 1 || nsub > 2 || !same_bwd_grid(ap, nsub)) return hipErrorInvalidValue;
   if (elem_bytes == 2) return launch_bwd_dq_bf16(ap, nsub, head_dim, st);
-  if (nsub != 1 || elem_bytes != 4) return hipErrorInvalidValue;
+  if (nsub != 1 || elem_bytes != 4 || ap[0].klen != ap[0].len) return hipErrorInvalidValue;
   const BwdArgs& a = ap[0];
   if (head_dim == 64) return launch_dq_t<float, 64, 32>(a, st);
   if (head_dim == 128) return launch_dq_t<float, 128, 32>(a, st);

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
   const int head = g * a.group + hs * a.hpw + w / wpr;
   const int row0 = rt * R + (w % wpr) * 32;
   const int wg_last_row = min(rt * R + R, a.len) - 1;
-  int ntiles = (a.len + BC - 1) / BC;
+  int ntiles = (a.klen + BC - 1) / BC;
   if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
 
   const size_t qstride = (size_t)a.hq * D;   // elements between query rows
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
   static_assert(St::NROW == C::KROW && St::TROW == C::VROW, "LDS pitches");
   St kst, vst;
   auto gload = [&](int t0) {
-    kst.load(kbase, kvstride, t0, a.len, tid);
-    vst.load(vbase, kvstride, t0, a.len, tid);
+    kst.load(kbase, kvstride, t0, a.klen, tid);
+    vst.load(vbase, kvstride, t0, a.klen, tid);
   };
   auto lstore = [&](int buf) {
     unsigned char* ks = smem + buf * C::STAGE;
@@ -148,15 +148,15 @@ __global__ __launch_bounds__(NW * 64) RA_FWD_OCC void fwd_step_kernel(FwdArgs a)
 #pragma unroll
         for (int ks_ = 0; ks_ < D / 16; ++ks_) mma(s[kt], frag_load<T>(krow + ks_ * 16), qf[ks_]);
       }
-      // masking: diagonal block (key > query) and ragged tail (key >= len)
+      // masking: diagonal block (key > query) and ragged tail (key >= klen)
       const int qi = row0 + n;
-      if ((a.diag && t0 + BC - 1 > row0) || (t0 + BC > a.len)) {
+      if ((a.diag && t0 + BC - 1 > row0) || (t0 + BC > a.klen)) {
 #pragma unroll
         for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = t0 + kt * 32 + crow(i, hf);
-            if (key >= a.len || (a.diag && key > qi)) s[kt][i] = kNegInf;
+            if (key >= a.klen || (a.diag && key > qi)) s[kt][i] = kNegInf;
           }
       }
       // online softmax (log2 domain)
@@ -253,7 +253,7 @@ __device__ __forceinline__ void fwd_bf16_tile(const FwdArgs& a, const unsigned c
   for (int r = 0; r < RG; ++r) {
     if constexpr (MASKED) {
       // visible keys of this lane's query: local key index <= lim
-      const int lim = (a.diag ? min(qi0 + 32 * r, a.len - 1) : a.len - 1) - t0;
+      const int lim = (a.diag ? min(qi0 + 32 * r, a.klen - 1) : a.klen - 1) - t0;
 #pragma unroll
       for (int kt = 0; kt < BC / 32; ++kt)
 #pragma unroll
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(ARG arg) {
   const int row0 = rt * R + (wu % wpr) * 32 * RG;  // this wave's first row (RG groups of 32)
   const int qi = row0 + n;
   const int wg_last_row = min(rt * R + R, a.len) - 1;
-  int ntiles = (a.len + BC - 1) / BC;
+  int ntiles = (a.klen + BC - 1) / BC;
   if (a.diag) ntiles = min(ntiles, wg_last_row / BC + 1);
 
   const size_t qstride = (size_t)a.hq * D, kvstride = (size_t)a.hkv * D;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(ARG arg) {
   auto issue = [&](int t0, unsigned char* kd) {  // kd: K tile, V tile follows
     unsigned char* vd = kd + TILEB;
     const size_t tb = (size_t)t0 * kvstride * 2;
-    if (t0 + BC <= a.len) {
+    if (t0 + BC <= a.klen) {
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
         const int q = wu * IPW + j;
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(ARG arg) {
       for (int j = 0; j < IPW; ++j) {
         const int q = wu * IPW + j;
         const int r = q * RPI + lrow;
-        const int row = min(t0 + r, a.len - 1);
+        const int row = min(t0 + r, a.klen - 1);
         const bf16_storage* ks = kbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
         const bf16_storage* vs = vbase + (size_t)row * kvstride + ((slot ^ swz<D>(r)) * 8);
         lds_dma16(ks, __builtin_amdgcn_readfirstlane(lds_addr(kd + q * 1024)));
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(ARG arg) {
   // tiles [0, nfull) need no mask for any wave of this workgroup; the rest
   // (diagonal band, ragged tail) take the masked instantiation
   const int wg_first_row = rt * R;
-  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.len / BC);
+  const int nfull = min(ntiles, a.diag ? (wg_first_row + 1) / BC : a.klen / BC);
   const LdsOperandOffsets<D> lo(lane, TILEB);
   // one unmasked tile; ST is its stage when known at compile time (then every
   // LDS read address is an offset register plus an immediate), else -1
@@ -468,11 +468,12 @@ constexpr int kF32Waves = kFwdWaves;
 #define RA_FWD_RG 1  // 32-row query groups per wave (2: 64 rows at one wave per SIMD)
 #endif
 
-// sub-problems of one launch must agree on the grid: same length and head layout
+// sub-problems of one launch must agree on the grid: same lengths and head layout.
+// A causal diagonal block pairs query row i with key i, so it needs as many keys as rows.
 template <typename A> static bool same_grid(const A* a, int nsub) {
-  for (int i = 1; i < nsub; ++i)
-    if (a[i].len != a[0].len || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv || a[i].hpw != a[0].hpw ||
-        a[i].hsub != a[0].hsub)
+  for (int i = 0; i < nsub; ++i)
+    if (a[i].len != a[0].len || a[i].klen != a[0].klen || a[i].hq != a[0].hq || a[i].hkv != a[0].hkv ||
+        a[i].hpw != a[0].hpw || a[i].hsub != a[0].hsub || (a[i].diag && a[i].klen != a[i].len))
       return false;
   return true;
 }

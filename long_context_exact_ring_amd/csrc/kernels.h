@@ -12,7 +12,8 @@ struct FwdArgs {
   const void* v;
   float* out;   // [len][hq][D] running output (overwritten when first != 0)
   float* lse;   // [hq][len] running log-sum-exp (natural log)
-  int len;      // block length (query rows = keys)
+  int len;      // query rows
+  int klen;     // keys (K/V rows); equal to len whenever diag is set
   int hq, hkv;
   int group;    // hq / hkv
   int hpw;      // query heads sharing one workgroup (divides group and the wave count)
@@ -54,18 +55,20 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, int elem_bytes, int head_dim, hip
 // to k16/v16, which the dQ kernel then reads as its k/v.
 struct BwdArgs {
   const void* q;     // [len][hq][D]
-  const void* k;     // [len][hkv][D]
+  const void* k;     // [klen][hkv][D]
   const void* v;
   const void* dout;  // [len][hq][D]
-  void* k16;         // bf16 dK/dV kernel: [len][hkv][D] half copy of k (written)
-  void* v16;         // bf16 dK/dV kernel: [len][hkv][D] half copy of v (written)
+  void* k16;         // bf16 dK/dV kernel: [klen][hkv][D] half copy of k (written)
+  void* v16;         // bf16 dK/dV kernel: [klen][hkv][D] half copy of v (written)
   const float* lse;  // [hq][len]
   const float* delta;  // [hq][len]
   const float* lse2;   // [hq][len] lse * log2(e)
   float* dq;         // [len][hq][D]   (overwrite when first != 0, else accumulate)
-  float* dk;         // [len][hkv][D]  (accumulate)
-  float* dv;         // [len][hkv][D]  (accumulate)
-  int len, hq, hkv, group;
+  float* dk;         // [klen][hkv][D] (accumulate)
+  float* dv;         // [klen][hkv][D] (accumulate)
+  int len;           // query rows
+  int klen;          // keys; equal to len whenever diag is set
+  int hq, hkv, group;
   int hpw, hsub;     // dQ kernel: query heads per workgroup (as FwdArgs)
   int diag;
   int first;

@@ -416,6 +416,55 @@ static float rsqrt_dim(int d) { return 1.0f / std::sqrt((float)d); }
 // (second half), so every rank's causal work is the same.
 static int zz_chunk(int block, int half, int n_blocks) { return half == 0 ? block : 2 * n_blocks - 1 - block; }
 
+// The (query half, key half) chunk pairs of one zig-zag round, grouped into
+// kernel sub-problems.  `own` is the side whose rows a sub-problem writes (the
+// query half for the forward and dQ, the key half for dK/dV), `other` the
+// side it streams.  When one `own` half sees both `other` halves and neither
+// pair is a causal diagonal, the two pairs become one sub-problem over the
+// whole other block (contiguous in memory), so a workgroup streams a
+// full-length block as in the contiguous layout.  The sub-problems are then
+// paired into launches: two per launch when they write different halves and
+// have the same lengths.
+struct ZzSpan {
+  int own, other0, n_other;  // n_other 2: both other halves, from half 0
+  bool diag;
+};
+struct ZzLaunch {
+  ZzSpan sub[2];
+  int nsub;
+};
+static std::vector<ZzLaunch> zz_launches(const Shape& sh, int j, bool own_is_query) {
+  std::vector<ZzSpan> sp[2];
+  for (int o = 0; o < 2; ++o) {
+    bool live[2], diag[2];
+    for (int t = 0; t < 2; ++t) {
+      const int u = own_is_query ? o : t, v = own_is_query ? t : o;  // query half u, key half v
+      const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
+      live[t] = !(sh.causal && kc > qc);  // a chunk wholly in the queries' future is skipped
+      diag[t] = sh.causal && kc == qc;
+    }
+    if (live[0] && live[1] && !diag[0] && !diag[1]) {
+      sp[o].push_back({o, 0, 2, false});
+    } else {
+      for (int t = 0; t < 2; ++t)
+        if (live[t]) sp[o].push_back({o, t, 1, diag[t]});
+    }
+  }
+  std::vector<ZzLaunch> out;
+  size_t i0 = 0, i1 = 0;
+  while (i0 < sp[0].size() || i1 < sp[1].size()) {
+    ZzLaunch l{};
+    if (i0 < sp[0].size()) {
+      l.sub[l.nsub++] = sp[0][i0++];
+      if (i1 < sp[1].size() && sp[1][i1].n_other == l.sub[0].n_other) l.sub[l.nsub++] = sp[1][i1++];
+    } else {
+      l.sub[l.nsub++] = sp[1][i1++];
+    }
+    out.push_back(l);
+  }
+  return out;
+}
+
 // Query heads that share one workgroup: the largest common divisor of the group
 // size and the wave count (each wave owns 32 rows of one head).
 static int heads_per_block(int group, int waves) {
@@ -446,6 +495,7 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   base.out = out;
   base.lse = lse;
   base.len = sh.block_len;
+  base.klen = sh.block_len;
   base.ls = sh.block_len;
   base.hq = sh.heads;
   base.hkv = sh.kv_heads;
@@ -466,30 +516,28 @@ int fwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       return RA_OK;
     }
     // zig-zag: query half u holds chunk zz_chunk(rank, u), key half v chunk zz_chunk(j, v).
-    // For each key half, the query halves that see it run as the two sub-problems of
-    // one launch (they write different rows); the key halves follow one another.
+    // Sub-problems of one launch write different query halves; those of one query half
+    // follow one another (the later ones merge into the earlier's output).
     const int h = sh.block_len / 2;
-    for (int v = 0; v < 2; ++v) {
+    for (const ZzLaunch& l : zz_launches(sh, j, true)) {
       FwdArgs sub[2];
-      int nsub = 0;
-      for (int u = 0; u < 2; ++u) {
-        const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
-        if (sh.causal && kc > qc) continue;  // every key of the chunk lies in the queries' future
-        FwdArgs& a = sub[nsub++];
+      for (int i = 0; i < l.nsub; ++i) {
+        const ZzSpan& z = l.sub[i];
+        FwdArgs& a = sub[i];
         a = base;
-        a.q = static_cast<const char*>(q) + (size_t)u * h * sh.heads * sh.head_dim * sh.elem_bytes;
-        a.out = out + (size_t)u * h * sh.heads * sh.head_dim;
-        a.lse = lse + (size_t)u * h;
-        a.k = static_cast<const char*>(kp) + (size_t)v * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
-        a.v = static_cast<const char*>(vp) + (size_t)v * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
+        a.q = static_cast<const char*>(q) + (size_t)z.own * h * sh.heads * sh.head_dim * sh.elem_bytes;
+        a.out = out + (size_t)z.own * h * sh.heads * sh.head_dim;
+        a.lse = lse + (size_t)z.own * h;
+        a.k = static_cast<const char*>(kp) + (size_t)z.other0 * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
+        a.v = static_cast<const char*>(vp) + (size_t)z.other0 * h * sh.kv_heads * sh.head_dim * sh.elem_bytes;
         a.len = h;
-        a.diag = (sh.causal && kc == qc) ? 1 : 0;
-        a.first = first_half[u] ? 1 : 0;
-        first_half[u] = false;
+        a.klen = z.n_other * h;
+        a.diag = z.diag ? 1 : 0;
+        a.first = first_half[z.own] ? 1 : 0;
+        first_half[z.own] = false;
       }
-      if (nsub == 0) continue;
       ProfScope ps(KIND_FWD, stream);
-      RA_HIP(launch_fwd_step(sub, nsub, sh.elem_bytes, sh.head_dim, stream));
+      RA_HIP(launch_fwd_step(sub, l.nsub, sh.elem_bytes, sh.head_dim, stream));
     }
     return RA_OK;
   };
@@ -569,6 +617,7 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
   base.lse2 = lse2;
   base.dq = dq;
   base.len = sh.block_len;
+  base.klen = sh.block_len;
   base.ls = sh.block_len;
   base.hq = sh.heads;
   base.hkv = sh.kv_heads;
@@ -612,57 +661,50 @@ int bwd_impl(const void* q, const void* const* kb, const void* const* vb, const 
       const BwdArgs b = for_dq(a);
       return launch_dq(&b, 1);
     }
-    // zig-zag: the (query half u, key half v) pairs that attend.  dK/dV launches take the
-    // key halves of one query half as two sub-problems (they write different dK/dV rows);
-    // dQ launches take the query halves of one key half (different dQ rows).  Every live
-    // key half is covered by some dK/dV launch, which writes its half copy before the
-    // dQ launches of the round read it.
+    // zig-zag: query half u holds chunk zz_chunk(rank, u), key half v chunk zz_chunk(j, v).
+    // dK/dV sub-problems of one launch write different key halves, dQ sub-problems
+    // different query halves.  Every live key half is covered by some dK/dV launch, which
+    // writes its half copy before the dQ launches of the round read it.
     const int h = sh.block_len / 2;
     const size_t qrow = (size_t)sh.heads * sh.head_dim, krow = (size_t)sh.kv_heads * sh.head_dim;
-    BwdArgs pa[2][2];
-    bool live[2][2];
-    for (int u = 0; u < 2; ++u)
-      for (int v = 0; v < 2; ++v) {
-        const int qc = zz_chunk(sh.rank, u, sh.n_blocks), kc = zz_chunk(j, v, sh.n_blocks);
-        live[u][v] = !(sh.causal && kc > qc);
-        BwdArgs& a = pa[u][v];
-        a = base;
-        a.q = static_cast<const char*>(qk) + u * h * qrow * sh.elem_bytes;
-        a.dout = static_cast<const char*>(dok) + u * h * qrow * sh.elem_bytes;
-        a.lse = lse + (size_t)u * h;
-        a.delta = delta + (size_t)u * h;
-        a.lse2 = lse2 + (size_t)u * h;
-        a.dq = dq + u * h * qrow;
-        a.k = static_cast<const char*>(kp) + v * h * krow * sh.elem_bytes;
-        a.v = static_cast<const char*>(vp) + v * h * krow * sh.elem_bytes;
-        a.k16 = half ? k16 + v * h * krow * 2 : nullptr;
-        a.v16 = half ? v16 + v * h * krow * 2 : nullptr;
-        a.dk = dkb[j] + v * h * krow;
-        a.dv = dvb[j] + v * h * krow;
-        a.len = h;
-        a.diag = (sh.causal && kc == qc) ? 1 : 0;
-      }
-    for (int u = 0; u < 2; ++u) {
+    // query halves [u0, u0 + nu) against key halves [v0, v0 + nv)
+    auto args = [&](int u0, int nu, int v0, int nv, bool diag) {
+      BwdArgs a = base;
+      a.q = static_cast<const char*>(qk) + u0 * h * qrow * sh.elem_bytes;
+      a.dout = static_cast<const char*>(dok) + u0 * h * qrow * sh.elem_bytes;
+      a.lse = lse + (size_t)u0 * h;
+      a.delta = delta + (size_t)u0 * h;
+      a.lse2 = lse2 + (size_t)u0 * h;
+      a.dq = dq + u0 * h * qrow;
+      a.k = static_cast<const char*>(kp) + v0 * h * krow * sh.elem_bytes;
+      a.v = static_cast<const char*>(vp) + v0 * h * krow * sh.elem_bytes;
+      a.k16 = half ? k16 + v0 * h * krow * 2 : nullptr;
+      a.v16 = half ? v16 + v0 * h * krow * 2 : nullptr;
+      a.dk = dkb[j] + v0 * h * krow;
+      a.dv = dvb[j] + v0 * h * krow;
+      a.len = nu * h;
+      a.klen = nv * h;
+      a.diag = diag ? 1 : 0;
+      return a;
+    };
+    for (const ZzLaunch& l : zz_launches(sh, j, false)) {  // own = key half
       BwdArgs sub[2];
-      int nsub = 0;
-      for (int v = 0; v < 2; ++v)
-        if (live[u][v]) sub[nsub++] = pa[u][v];
-      if (nsub == 0) continue;
-      int st2 = launch_dkdv(sub, nsub);
+      for (int i = 0; i < l.nsub; ++i) {
+        const ZzSpan& z = l.sub[i];
+        sub[i] = args(z.other0, z.n_other, z.own, 1, z.diag);
+      }
+      int st2 = launch_dkdv(sub, l.nsub);
       if (st2 != RA_OK) return st2;
     }
-    for (int v = 0; v < 2; ++v) {
+    for (const ZzLaunch& l : zz_launches(sh, j, true)) {  // own = query half
       BwdArgs sub[2];
-      int nsub = 0;
-      for (int u = 0; u < 2; ++u)
-        if (live[u][v]) {
-          BwdArgs& a = sub[nsub++];
-          a = for_dq(pa[u][v]);
-          a.first = first_half[u] ? 1 : 0;  // dQ rows of half u: written by the first, then accumulated
-          first_half[u] = false;
-        }
-      if (nsub == 0) continue;
-      int st2 = launch_dq(sub, nsub);
+      for (int i = 0; i < l.nsub; ++i) {
+        const ZzSpan& z = l.sub[i];
+        sub[i] = for_dq(args(z.own, 1, z.other0, z.n_other, z.diag));
+        sub[i].first = first_half[z.own] ? 1 : 0;  // dQ rows of half u: written by the first, then accumulated
+        first_half[z.own] = false;
+      }
+      int st2 = launch_dq(sub, l.nsub);
       if (st2 != RA_OK) return st2;
     }
     return RA_OK;

@@ -99,17 +99,37 @@ def test_zigzag_every_rank_runs_the_same_steps():
         finally:
             ra.ring_attn_profile_enable(False)
         counts.append(recs["fwd_step"][1])
-    log(f"  half-size forward launches per rank: {counts}")
+    log(f"  zig-zag forward launches per rank: {counts}")
     # Chunk pairs (query chunk qc, key chunk kc) that attend: kc <= qc.  Block b holds chunks
-    # b and 2D-1-b.  Every rank has 2D+1 of them (3 in its diagonal round, 2 in every other),
-    # and the library launches the query halves that see one key half together.
+    # b and 2D-1-b.  Every rank has 2D+1 of them (3 in its diagonal round, 2 in every other).
+    # A query half that sees both key halves off the diagonal runs them as one sub-problem;
+    # sub-problems of the two query halves share a launch when their key spans match.
     zz = lambda b, half: b if half == 0 else 2 * D - 1 - b
     pairs, launches = [], []
     for r in range(D):
-        live = [[zz(j, v) <= zz(r, u) for u in (0, 1) for v in (0, 1)] for j in range(D)]
-        pairs.append(sum(map(sum, live)))
-        launches.append(sum(int(l[0 * 2 + v] or l[1 * 2 + v]) for l in live for v in (0, 1)))
-    assert pairs == [2 * D + 1] * D
+        n_launch = 0
+        for j in range(D):
+            subs = []
+            for u in (0, 1):
+                live = [zz(j, v) <= zz(r, u) for v in (0, 1)]
+                diag = [zz(j, v) == zz(r, u) for v in (0, 1)]
+                pairs.append((r, sum(live)))
+                subs.append([2] if all(live) and not any(diag) else [1 for v in (0, 1) if live[v]])
+            # greedy pairing in order: the i-th sub-problems of the two halves pair if both exist
+            # and span the same number of key halves
+            a, b = subs
+            i = k = 0
+            while i < len(a) or k < len(b):
+                if i < len(a) and k < len(b) and a[i] == b[k]:
+                    i, k = i + 1, k + 1
+                elif i < len(a):
+                    i += 1
+                else:
+                    k += 1
+                n_launch += 1
+        launches.append(n_launch)
+    assert [sum(n for rr, n in pairs if rr == r) for r in range(D)] == [2 * D + 1] * D
+    assert launches == [D + 1] * D  # one launch per round, two in the diagonal round
     assert counts == launches
 
 
