@@ -4,7 +4,8 @@ The whole sequence is drawn once; block b of the ring is chunk b followed by
 chunk 2D-1-b.  Every rank runs the zig-zag forward and backward; results are
 put back in sequence order and compared with dense fp64 causal attention.
 The per-rank launch counts show the balance: every rank runs the same
-number of half-size steps.
+number of steps.  Without a mask the layout is only a permutation of the
+sequence, and the results equal plain attention.
 
 The shapes include large gradients: under the causal mask key 0 collects
 weight from every row of every grouped head, so a 4-way group over 600 rows
@@ -45,10 +46,16 @@ def _seq(seed, S, hq, hkv, d):
     return q, k, v, do
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+# without a mask every query chunk sees both key chunks of every block, so each round runs as
+# whole-block sub-problems on both sides
+NONCAUSAL_CASES = [(128, 4, 2, 200, 3, False), (64, 2, 2, 66, 4, False)]
+
+
+@pytest.mark.parametrize("case", [c + (True,) for c in CASES] + NONCAUSAL_CASES,
+                         ids=lambda c: "-".join(map(str, c)))
 def test_zigzag_fwd_bwd_all_ranks(case):
     require_gpu()
-    d, hq, hkv, c, D = case
+    d, hq, hkv, c, D, causal = case
     log(f"zigzag case {case}")
     S = c * D
     q, k, v, do = _seq(83, S, hq, hkv, d)
@@ -62,8 +69,8 @@ def test_zigzag_fwd_bwd_all_ranks(case):
     dq = np.zeros((S, hq, d))
     for r in range(D):
         qd, dod = dev(q[pos[r]], "bf16"), dev(do[pos[r]], "bf16")
-        o, l = ra.fwd(qd, kb, vb, causal=True, rank=r, zigzag=True)
-        g, _, _ = ra.bwd(qd, kb, vb, o, dod, l, causal=True, rank=r, dk_blocks=dkb, dv_blocks=dvb, zigzag=True)
+        o, l = ra.fwd(qd, kb, vb, causal=causal, rank=r, zigzag=True)
+        g, _, _ = ra.bwd(qd, kb, vb, o, dod, l, causal=causal, rank=r, dk_blocks=dkb, dv_blocks=dvb, zigzag=True)
         torch.cuda.synchronize()
         out[pos[r]] = o.cpu().numpy()
         lse[:, pos[r]] = l.cpu().numpy()
@@ -73,7 +80,7 @@ def test_zigzag_fwd_bwd_all_ranks(case):
     for b in range(D):
         dk[pos[b]] = dkb[b].cpu().numpy()
         dv[pos[b]] = dvb[b].cpu().numpy()
-    dq_ref, dk_ref, dv_ref, o_ref, l_ref = oracle.attention_bwd(q, k, v, do, causal=True)
+    dq_ref, dk_ref, dv_ref, o_ref, l_ref = oracle.attention_bwd(q, k, v, do, causal=causal)
     compare("out", out, o_ref, "bf16")
     compare("lse", lse, l_ref, "bf16")
     compare("dq", dq, dq_ref, "bf16")
